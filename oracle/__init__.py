@@ -1,0 +1,1 @@
+"""FP64 CPU oracle (test infrastructure only; never imported by the product package)."""

@@ -1,0 +1,132 @@
+"""Plain FP64 CPU oracle for the deterministic DSA lightning-indexer top-k scan.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the CPU-baseline leg
+of the benchmark may import or run this module.  The product package never
+imports it, and it shares no code, table or helper with the HIP path.
+
+Sources ("P1" below is flashinfer PR #8691, "perf(cake_dsa_indexer_det):
+ticket scheduling on sm_107a, no fill kernel in eager entry"; "P3" is
+flashinfer PR #4573, "feat(cake_sparse_mla): support SM100 and SM103"):
+
+* Types and result (P1, description): queries and keys are BF16, head weights
+  and scores FP32; for each query the scan returns the ids of its top-k keys;
+  ids and scores must not depend on how the work is partitioned or chunked;
+  equal scores are ordered by the larger id.
+* What is scored (P1, the vendoring commit message naming the package's job
+  as lightning-indexer scores plus deterministic exact top-k).  The pages do
+  not print the formula; the oracle adopts the standard lightning-indexer
+  definition
+        I[t, s] = sum_h  w[t, h] * max(0, sum_d q[t, h, d] * k[s, d])
+  with no extra scale (w carries any 1/sqrt(H)).
+* Segments and causality (P1, eager-entry tables: "single causal document",
+  "CP tail", "CP16 zigzag rank 0", "split tail" rows; and the causal query
+  offsets the eager entry takes, commit message on the placeholder offsets):
+  segment b holds queries cu_q[b]..cu_q[b+1]-1 and keys cu_k[b]..cu_k[b+1]-1;
+  query t at position p = off[b] + (t - cu_q[b]) sees the first
+  min(max(p+1, 0), len_k) keys of its segment (inclusive diagonal; positions
+  past the segment end see the whole segment).
+* Ids are global row indices into k.  Rows with fewer than k visible keys
+  are padded with id -1 (the consumer's "no key" marker, P3 follow-up PRs on
+  sparse-index consumption), and score -inf.
+* Output order within a row: ascending id.
+
+Readings where the pages are silent are listed in the design notes of the
+repository (formula, inclusive diagonal, per-segment offsets, global ids,
+ascending order, -inf padding score).
+
+Everything here is FP64: BF16 and FP32 inputs convert to FP64 exactly, the
+dot products use a library matmul, the head reduction a library
+matrix-vector product, and the selection a library lexicographic sort on
+(score descending, id descending).  No blocking, fusion or reordering beyond
+that.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NEG_INF = float("-inf")
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Exact BF16 -> FP64: a BF16 value is the upper half of an FP32 word."""
+    b = np.ascontiguousarray(np.asarray(bits).astype(np.uint16)).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def from_torch(q, k, w):
+    """Convert torch CPU tensors (q, k BF16; w FP32) into exact FP64 arrays."""
+    import torch  # local: the oracle itself only needs numpy
+    qb = q.contiguous().view(torch.int16).numpy().view(np.uint16)
+    kb = k.contiguous().view(torch.int16).numpy().view(np.uint16)
+    return bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), w.double().numpy()
+
+
+def segment_of(cu_q: np.ndarray, t: int) -> int:
+    """Index b of the segment holding query t (empty segments are skipped)."""
+    return int(np.searchsorted(np.asarray(cu_q), t, side="right") - 1)
+
+
+def visible(cu_q, cu_k, offs, t: int):
+    """(first global key id, number of visible keys) for query t."""
+    cu_q = np.asarray(cu_q, dtype=np.int64)
+    cu_k = np.asarray(cu_k, dtype=np.int64)
+    b = segment_of(cu_q, t)
+    o = 0 if offs is None else int(np.asarray(offs)[b])
+    p = o + (t - int(cu_q[b]))
+    len_k = int(cu_k[b + 1] - cu_k[b])
+    n = min(max(p + 1, 0), len_k)
+    return int(cu_k[b]), n
+
+
+def row_scores(q64: np.ndarray, k64: np.ndarray, w64: np.ndarray, t: int, first: int, n: int) -> np.ndarray:
+    """I[t, s] for the n keys s = first .. first+n-1, in FP64."""
+    if n == 0:
+        return np.zeros(0, dtype=np.float64)
+    S = q64[t] @ k64[first:first + n].T          # [H, n]: per-head dot products
+    return w64[t] @ np.maximum(S, 0.0)           # sum_h w[t,h] * ReLU(S[h, :])
+
+
+def select_topk(scores: np.ndarray, ids: np.ndarray, topk: int):
+    """Top-k under the total order (score desc, id desc); ids returned ascending, padded."""
+    n = len(ids)
+    m = min(topk, n)
+    order = np.lexsort((-ids.astype(np.int64), -scores))   # primary: -score, secondary: -id
+    take = order[:m]
+    sel_ids = ids[take]
+    sel_scores = scores[take]
+    asc = np.argsort(sel_ids, kind="stable")
+    out_ids = np.full(topk, -1, dtype=np.int64)
+    out_scores = np.full(topk, NEG_INF, dtype=np.float64)
+    out_ids[:m] = sel_ids[asc]
+    out_scores[:m] = sel_scores[asc]
+    return out_ids, out_scores
+
+
+def topk_rows(q64, k64, w64, cu_q, cu_k, offs, topk: int, rows=None):
+    """Oracle result for the given query rows (all rows if None).
+
+    Returns (ids int64 [R, topk], scores f64 [R, topk], detail) where detail[r]
+    holds the row's full visible score vector and first id, for tolerance checks.
+    """
+    T = q64.shape[0]
+    rows = range(T) if rows is None else rows
+    rows = list(rows)
+    ids_out = np.full((len(rows), topk), -1, dtype=np.int64)
+    sc_out = np.full((len(rows), topk), NEG_INF, dtype=np.float64)
+    detail = []
+    for r, t in enumerate(rows):
+        first, n = visible(cu_q, cu_k, offs, t)
+        s = row_scores(q64, k64, w64, t, first, n)
+        ids = np.arange(first, first + n, dtype=np.int64)
+        ids_out[r], sc_out[r] = select_topk(s, ids, topk)
+        detail.append((first, s))
+    return ids_out, sc_out, detail
+
+
+def topk_workload(wl, rows=None):
+    """Oracle on a generated workload (torch CPU tensors)."""
+    q64, k64, w64 = from_torch(wl.q, wl.k, wl.w)
+    cu_q = wl.cu_seqlens_q.numpy()
+    cu_k = wl.cu_seqlens_k.numpy()
+    offs = None if wl.q_pos_offsets is None else wl.q_pos_offsets.numpy()
+    return topk_rows(q64, k64, w64, cu_q, cu_k, offs, wl.topk, rows)
