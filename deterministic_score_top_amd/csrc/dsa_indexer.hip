@@ -1,0 +1,318 @@
+// Host side of the C ABI declared in include/dsa_indexer.h.
+//
+// Argument validation is host-only (it never reads device memory and never synchronises);
+// each call enqueues exactly two kernels on the caller's stream -- the persistent score
+// kernel and the per-row select kernel -- and nothing else: no allocation, no memset, no
+// fill kernel (the eager entry of flashinfer PR #8691 launches only the scan's kernels).
+
+#include "dsa_indexer.h"
+
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string.h>
+#include <vector>
+
+#include "dsa_internal.h"
+
+namespace {
+
+struct DeviceInfo {
+  bool ok = false;
+  int cus = 0;
+  int score_blocks_per_cu = 0;  // at the smem limit (a lower bound for smaller tables)
+};
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_once[kMaxDevices];
+DeviceInfo g_info[kMaxDevices];
+
+const DeviceInfo* device_info() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_once[dev], [dev]() {
+    DeviceInfo info;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return;
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return;
+    info.cus = prop.multiProcessorCount;
+    if (dsa::score_prepare(dsa::score_smem_limit()) != hipSuccess) return;
+    int bpc = 0;
+    if (dsa::score_occupancy(&bpc, dsa::score_smem_limit()) != hipSuccess || bpc < 1) return;
+    info.score_blocks_per_cu = bpc;
+    info.ok = true;
+    g_info[dev] = info;
+  });
+  return g_info[dev].ok ? &g_info[dev] : nullptr;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int64_t lmax_of(const dsa_indexer_shape* s) {
+  int64_t L = s->max_seqlen_k > 0 ? s->max_seqlen_k : s->total_k;
+  if (L > dsa::kMaxSeqlenK) L = dsa::kMaxSeqlenK;
+  if (L < 1) L = 1;
+  return L;
+}
+
+int64_t row_stride(const dsa_indexer_shape* s) {
+  return (lmax_of(s) + dsa::kRowAlign - 1) / dsa::kRowAlign * dsa::kRowAlign;
+}
+
+int check_shape(const dsa_indexer_shape* s) {
+  if (!s) return DSA_ERR_NULL;
+  if (s->num_segments < 1 || s->total_q < 0 || s->total_k < 0) return DSA_ERR_SHAPE;
+  if (s->num_heads != dsa::kHeads || s->head_dim != dsa::kDim) return DSA_ERR_SHAPE;
+  if (s->max_seqlen_k < 0 || s->max_seqlen_k > dsa::kMaxSeqlenK) return DSA_ERR_SHAPE;
+  return DSA_OK;
+}
+
+int max_tiles_of(const dsa_indexer_shape* s) {
+  return (s->total_q + dsa::kTileQueries - 1) / dsa::kTileQueries + s->num_segments;
+}
+
+struct Call {
+  const dsa_indexer_shape* shape;
+  const void* q;
+  const void* k;
+  const float* w;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* offs;
+  float* score_out;
+  int64_t ld;
+  uint32_t* ctrl;
+  const dsa_indexer_tuning* tuning;
+};
+
+int launch_scores(const Call& c, hipStream_t stream) {
+  const DeviceInfo* dev = device_info();
+  if (!dev) return DSA_ERR_DEVICE;
+  const dsa_indexer_shape* s = c.shape;
+  const int max_tiles = max_tiles_of(s);
+  const size_t smem = dsa::score_smem_bytes(s->num_segments, max_tiles);
+  if (smem > dsa::score_smem_limit()) return DSA_ERR_SHAPE;
+
+  const int64_t L = lmax_of(s);
+  const int grid_default = dev->cus * dev->score_blocks_per_cu;
+  int grid = grid_default;
+  int chunk = 0;
+  if (c.tuning) {
+    if (c.tuning->grid_blocks < 0 || c.tuning->key_chunk_tiles < 0) return DSA_ERR_SHAPE;
+    if (c.tuning->grid_blocks > 0) grid = c.tuning->grid_blocks;
+    chunk = c.tuning->key_chunk_tiles;
+  }
+  if (chunk == 0) {
+    // about four units per resident block, chunks of at most 16 key tiles (1024 keys)
+    const int64_t key_tiles = (L + dsa::kTileKeys - 1) / dsa::kTileKeys;
+    const int64_t work = (int64_t)max_tiles * key_tiles;
+    int64_t ct = work / (4 * (int64_t)grid_default);
+    if (ct < 1) ct = 1;
+    if (ct > 16) ct = 16;
+    chunk = (int)ct;
+  }
+  if ((int64_t)chunk * dsa::kTileKeys > (int64_t)1 << 30) return DSA_ERR_SHAPE;
+
+  dsa::ScoreParams p;
+  p.q = static_cast<const uint16_t*>(c.q);
+  p.k = static_cast<const uint16_t*>(c.k);
+  p.w = c.w;
+  p.cu_q = c.cu_q;
+  p.cu_k = c.cu_k;
+  p.offs = c.offs;
+  p.out = c.score_out;
+  p.ld = c.ld;
+  p.ctrl = c.ctrl;
+  p.B = s->num_segments;
+  p.T = s->total_q;
+  p.Tkv = s->total_k;
+  p.Lmax = (int32_t)L;
+  p.chunk_tiles = chunk;
+  p.max_tiles = max_tiles;
+  if (dsa::launch_score(p, grid, smem, stream) != hipSuccess) return DSA_ERR_LAUNCH;
+  return DSA_OK;
+}
+
+int check_common(const dsa_indexer_shape* shape, const void* q, const void* k, const float* w,
+                 const int32_t* cu_q, const int32_t* cu_k, const int32_t* offs,
+                 const void* workspace) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!q || !k || !w || !cu_q || !cu_k || !workspace) return DSA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(w) || !aligned16(workspace)) return DSA_ERR_ALIGN;
+  if (!aligned4(cu_q) || !aligned4(cu_k) || (offs && !aligned4(offs))) return DSA_ERR_ALIGN;
+  return DSA_OK;
+}
+
+}  // namespace
+
+struct dsa_indexer_profiler {
+  int capacity = 0;
+  int used = 0;
+  std::vector<hipEvent_t> ev;  // 3 per slot: before score, between, after select
+};
+
+extern "C" {
+
+size_t dsa_indexer_workspace_size(const dsa_indexer_shape* shape) {
+  if (check_shape(shape) != DSA_OK) return 0;
+  return (size_t)dsa::kCtrlBytes + (size_t)shape->total_q * (size_t)row_stride(shape) * 4u;
+}
+
+int dsa_indexer_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!workspace) return DSA_ERR_NULL;
+  if (!aligned16(workspace)) return DSA_ERR_ALIGN;
+  if (workspace_bytes < (size_t)dsa::kCtrlBytes) return DSA_ERR_WORKSPACE;
+  if (!device_info()) return DSA_ERR_DEVICE;
+  if (dsa::launch_ctrl_init(static_cast<uint32_t*>(workspace), stream) != hipSuccess)
+    return DSA_ERR_LAUNCH;
+  return DSA_OK;
+}
+
+int dsa_indexer_topk_ex(const dsa_indexer_shape* shape, const void* q, const void* k,
+                        const float* w, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        const int32_t* q_pos_offsets, int32_t topk, int32_t* out_ids,
+                        float* out_scores, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream, const dsa_indexer_tuning* tuning,
+                        dsa_indexer_profiler* profiler) {
+  int rc = check_common(shape, q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets, workspace);
+  if (rc) return rc;
+  if (topk < 1 || topk > dsa::kMaxTopk) return DSA_ERR_SHAPE;
+  if (!out_ids || !out_scores) return DSA_ERR_NULL;
+  if (!aligned16(out_ids) || !aligned16(out_scores)) return DSA_ERR_ALIGN;
+  if (workspace_bytes < dsa_indexer_workspace_size(shape)) return DSA_ERR_WORKSPACE;
+  if (!device_info()) return DSA_ERR_DEVICE;
+  if (profiler && profiler->used >= profiler->capacity) return DSA_ERR_SHAPE;
+  if (shape->total_q == 0) return DSA_OK;
+
+  uint32_t* ctrl = static_cast<uint32_t*>(workspace);
+  float* scores = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + dsa::kCtrlBytes);
+  const int64_t ld = row_stride(shape);
+  hipEvent_t* ev = profiler ? &profiler->ev[3 * profiler->used] : nullptr;
+
+  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return DSA_ERR_LAUNCH;
+  Call c{shape, q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets, scores, ld, ctrl, tuning};
+  rc = launch_scores(c, stream);
+  if (rc) return rc;
+  if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return DSA_ERR_LAUNCH;
+
+  dsa::SelectParams sp;
+  sp.scores = scores;
+  sp.ld = ld;
+  sp.cu_q = cu_seqlens_q;
+  sp.cu_k = cu_seqlens_k;
+  sp.offs = q_pos_offsets;
+  sp.out_ids = out_ids;
+  sp.out_scores = out_scores;
+  sp.ctrl = ctrl;
+  sp.B = shape->num_segments;
+  sp.T = shape->total_q;
+  sp.Tkv = shape->total_k;
+  sp.Lmax = (int32_t)lmax_of(shape);
+  sp.topk = topk;
+  if (dsa::launch_select(sp, stream) != hipSuccess) return DSA_ERR_LAUNCH;
+  if (ev) {
+    if (hipEventRecord(ev[2], stream) != hipSuccess) return DSA_ERR_LAUNCH;
+    profiler->used++;
+  }
+  return DSA_OK;
+}
+
+int dsa_indexer_topk(const dsa_indexer_shape* shape, const void* q, const void* k, const float* w,
+                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                     const int32_t* q_pos_offsets, int32_t topk, int32_t* out_ids,
+                     float* out_scores, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  return dsa_indexer_topk_ex(shape, q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets, topk,
+                             out_ids, out_scores, workspace, workspace_bytes, stream, nullptr,
+                             nullptr);
+}
+
+int dsa_indexer_scores(const dsa_indexer_shape* shape, const void* q, const void* k,
+                       const float* w, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                       const int32_t* q_pos_offsets, float* out_scores, int64_t ld_out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_common(shape, q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets, workspace);
+  if (rc) return rc;
+  if (!out_scores) return DSA_ERR_NULL;
+  if (!aligned16(out_scores)) return DSA_ERR_ALIGN;
+  if (ld_out < lmax_of(shape) || (ld_out & 3)) return DSA_ERR_SHAPE;
+  if (workspace_bytes < (size_t)dsa::kCtrlBytes) return DSA_ERR_WORKSPACE;
+  if (shape->total_q == 0) return DSA_OK;
+  Call c{shape, q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets, out_scores, ld_out,
+         static_cast<uint32_t*>(workspace), nullptr};
+  return launch_scores(c, stream);
+}
+
+const char* dsa_indexer_status_string(int code) {
+  switch (code) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_NULL: return "a required pointer is NULL";
+    case DSA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case DSA_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case DSA_ERR_WORKSPACE: return "workspace too small";
+    case DSA_ERR_LAUNCH: return "HIP launch failed (re-initialise the workspace)";
+    case DSA_ERR_DEVICE: return "current device is not gfx950";
+    default: return "unknown status";
+  }
+}
+
+int dsa_indexer_profiler_create(int32_t capacity, dsa_indexer_profiler** out) {
+  if (!out) return DSA_ERR_NULL;
+  if (capacity < 1) return DSA_ERR_SHAPE;
+  dsa_indexer_profiler* p = new dsa_indexer_profiler();
+  p->capacity = capacity;
+  p->ev.resize((size_t)capacity * 3);
+  for (auto& e : p->ev) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+      dsa_indexer_profiler_destroy(p);
+      return DSA_ERR_DEVICE;
+    }
+  }
+  *out = p;
+  return DSA_OK;
+}
+
+int dsa_indexer_profiler_destroy(dsa_indexer_profiler* prof) {
+  if (!prof) return DSA_ERR_NULL;
+  for (auto& e : prof->ev)
+    if (e) hipEventDestroy(e);
+  delete prof;
+  return DSA_OK;
+}
+
+int dsa_indexer_profiler_read(dsa_indexer_profiler* prof, double* score_ms, double* select_ms,
+                              int32_t* calls) {
+  if (!prof || !score_ms || !select_ms || !calls) return DSA_ERR_NULL;
+  double a = 0.0, b = 0.0;
+  for (int i = 0; i < prof->used; ++i) {
+    hipEvent_t* e = &prof->ev[3 * i];
+    if (hipEventSynchronize(e[2]) != hipSuccess) return DSA_ERR_LAUNCH;
+    float x = 0.f, y = 0.f;
+    if (hipEventElapsedTime(&x, e[0], e[1]) != hipSuccess) return DSA_ERR_LAUNCH;
+    if (hipEventElapsedTime(&y, e[1], e[2]) != hipSuccess) return DSA_ERR_LAUNCH;
+    a += x;
+    b += y;
+  }
+  *score_ms = a;
+  *select_ms = b;
+  *calls = prof->used;
+  prof->used = 0;
+  return DSA_OK;
+}
+
+int dsa_indexer_read_status(const void* workspace, hipStream_t stream, uint32_t* status,
+                            uint32_t* ticket, uint32_t* done) {
+  if (!workspace || !status || !ticket || !done) return DSA_ERR_NULL;
+  if (hipStreamSynchronize(stream) != hipSuccess) return DSA_ERR_LAUNCH;
+  uint32_t h[4] = {0, 0, 0, 0};
+  if (hipMemcpy(h, workspace, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return DSA_ERR_LAUNCH;
+  *ticket = h[dsa::kCtrlTicket];
+  *done = h[dsa::kCtrlDone];
+  *status = h[dsa::kCtrlStatus];
+  return DSA_OK;
+}
+
+}  // extern "C"

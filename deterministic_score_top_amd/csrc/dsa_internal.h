@@ -1,0 +1,70 @@
+// Internal declarations shared by the library's translation units (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+constexpr int kHeads = 64;       // indexer heads H
+constexpr int kDim = 128;        // head dim D
+constexpr int kScoreThreads = 256;
+constexpr int kWaves = kScoreThreads / 64;
+constexpr int kQueriesPerWave = 2;
+constexpr int kTileQueries = kWaves * kQueriesPerWave;  // queries per work unit (8)
+constexpr int kTileKeys = 64;                            // keys per LDS stage
+constexpr int kCtrlBytes = 256;                          // control block at workspace offset 0
+constexpr int kMaxTopk = 2048;
+constexpr int kMaxSeqlenK = 65536;
+constexpr int kRowAlign = 64;                            // score rows padded to 64 floats
+
+// Control block layout (u32 words at workspace offset 0).
+constexpr int kCtrlTicket = 0;
+constexpr int kCtrlDone = 1;
+constexpr int kCtrlStatus = 2;
+
+constexpr uint32_t kStatusCorruptCounter = 0x1u;
+constexpr uint32_t kStatusBadSegments = 0x2u;
+constexpr uint32_t kStatusSeqlenBound = 0x4u;
+
+struct ScoreParams {
+  const uint16_t* q;  // bf16 [T, H, D]
+  const uint16_t* k;  // bf16 [Tkv, D]
+  const float* w;     // fp32 [T, H]
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* offs;  // may be null
+  float* out;           // fp32 rows, stride ld
+  int64_t ld;
+  uint32_t* ctrl;
+  int32_t B, T, Tkv, Lmax;
+  int32_t chunk_tiles;  // keys per unit = chunk_tiles * kTileKeys
+  int32_t max_tiles;    // capacity of the LDS tile table
+};
+
+struct SelectParams {
+  const float* scores;  // fp32 rows, stride ld
+  int64_t ld;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* offs;
+  int32_t* out_ids;
+  float* out_scores;
+  const uint32_t* ctrl;
+  int32_t B, T, Tkv, Lmax, topk;
+};
+
+// Dynamic LDS bytes of the score kernel for a tile table of `max_tiles` entries.
+size_t score_smem_bytes(int B, int max_tiles);
+size_t score_smem_limit();
+hipError_t score_prepare(size_t max_smem);
+hipError_t score_occupancy(int* blocks_per_cu, size_t smem);
+hipError_t launch_score(const ScoreParams& p, int grid, size_t smem, hipStream_t s);
+
+// Select kernel variant by the longest row it must hold in registers.
+hipError_t launch_select(const SelectParams& p, hipStream_t s);
+
+hipError_t launch_ctrl_init(uint32_t* ctrl, hipStream_t s);
+
+}  // namespace dsa

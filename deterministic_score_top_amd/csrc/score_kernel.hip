@@ -1,0 +1,345 @@
+// Score phase of the DSA indexer top-k scan on gfx950 (CDNA4).
+//
+// Computes I[t, s] = sum_h w[t, h] * max(0, q[t, h, :] . k[s, :]) for every causally visible
+// (query, key) pair of every segment and writes it to a dense FP32 row per query
+// (out[t * ld + j], j = segment-local key index).  Score definition: the lightning-indexer
+// form the scan of flashinfer PR #8691 (description; vendoring note) is built on.
+//
+// Work decomposition.  A work unit is (segment, tile of 8 consecutive queries, chunk of
+// keys).  The grid is persistent: every block draws unit numbers from a counter in the
+// workspace (the ticket word of the same page's description: blocks that are resident take
+// the next unit, so a foreign kernel holding some CUs does not push units into a second
+// wave).  Units are numbered segment by segment, and inside a segment from the last query
+// tile (most visible keys) to the first, so the cheapest units run last.  The last block to
+// leave resets the counter, so steady-state calls pay no reset.
+//
+// Inside a unit (256 threads, 4 waves, 2 queries per wave):
+//   * each wave holds the BF16 A operand of its 2 queries x 64 heads x 128 dims in VGPRs
+//     (8 row blocks of 16 rows x 4 K-steps of 32), loaded once per unit;
+//   * 64-key tiles of k are staged in LDS (double buffered, 16-byte chunks XOR-swizzled by
+//     key so the B-operand reads and the tile writes are bank-conflict free);
+//   * per 16-key column block: 32 v_mfma_f32_16x16x32_bf16 (FP32 accumulate, d ascending);
+//   * epilogue in registers: lane (group G = lane/16) holds heads 32*(G&1) + 0..31 of query
+//     G>>1 for key lane&15; it sums w*ReLU over its 32 heads in ascending head order with
+//     FMA, then adds the other half from lane^16.  The instruction sequence per (t, s) is the
+//     same in every unit, tile position and chunking, so scores are bit-reproducible.
+//
+// Row mapping of the A operand (row m of row block rb, held in the accumulators by lane
+// group m/4): query (m/4)>>1, head 32*((m/4)&1) + 4*rb + (m&3).
+
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kKBufBytes = kTileKeys * kDim * 2;  // one staged key tile: 16 KiB
+constexpr int kSlotInts = 16;
+constexpr int kPartEntries = kScoreThreads + 4;
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
+
+// First index in arr[0..n) whose value exceeds x (arr non-decreasing).
+__device__ __forceinline__ int upper_bound_u32(const uint32_t* arr, int n, uint32_t x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (arr[mid] <= x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// In-place exclusive scan of arr[0..n) by the block; arr[n] receives the total.
+__device__ void block_scan_excl(uint32_t* arr, int n, uint32_t* part) {
+  const int tid = threadIdx.x;
+  const int per = (n + kScoreThreads - 1) / kScoreThreads;
+  const int beg = min(tid * per, n);
+  const int end = min(beg + per, n);
+  uint32_t s = 0;
+  for (int i = beg; i < end; ++i) s += arr[i];
+  part[tid] = s;
+  __syncthreads();
+  if (tid < 64) {
+    const uint32_t a0 = part[4 * tid], a1 = part[4 * tid + 1], a2 = part[4 * tid + 2],
+                   a3 = part[4 * tid + 3];
+    const uint32_t sum = a0 + a1 + a2 + a3;
+    uint32_t inc = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(inc, o, 64);
+      if (tid >= o) inc += y;
+    }
+    const uint32_t ex = inc - sum;
+    part[4 * tid] = ex;
+    part[4 * tid + 1] = ex + a0;
+    part[4 * tid + 2] = ex + a0 + a1;
+    part[4 * tid + 3] = ex + a0 + a1 + a2;
+    if (tid == 63) part[kScoreThreads] = inc;
+  }
+  __syncthreads();
+  uint32_t run = part[tid];
+  for (int i = beg; i < end; ++i) {
+    const uint32_t v = arr[i];
+    arr[i] = run;
+    run += v;
+  }
+  if (tid == 0) arr[n] = part[kScoreThreads];
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* const kbuf0 = smem;
+  unsigned char* const kbuf1 = smem + kKBufBytes;
+  int* const slot = reinterpret_cast<int*>(smem + 2 * kKBufBytes);
+  uint32_t* const part = reinterpret_cast<uint32_t*>(slot + kSlotInts);
+  uint32_t* const seg_tp = part + kPartEntries;                   // B + 1 entries
+  uint32_t* const unit_pf = seg_tp + ((p.B + 1 + 3) & ~3);        // max_tiles + 1 entries
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int B = p.B;
+  const int chunk_keys = p.chunk_tiles * kTileKeys;
+
+  // ---- per-block plan: validate segments, tiles per segment, units per tile -------------
+  if (tid == 0) slot[2] = 0;
+  __syncthreads();
+  {
+    int flags = 0;
+    for (int b = tid; b <= B; b += kScoreThreads) {
+      const int cq = p.cu_q[b], ck = p.cu_k[b];
+      if (b == 0 && (cq != 0 || ck != 0)) flags |= 1;
+      if (b == B && (cq != p.T || ck != p.Tkv)) flags |= 1;
+      if (b < B) {
+        const int lq = p.cu_q[b + 1] - cq, lk = p.cu_k[b + 1] - ck;
+        if (lq < 0 || lk < 0) flags |= 1;
+        if (lk > p.Lmax) flags |= 2;
+        seg_tp[b] = lq > 0 ? (uint32_t)ceil_div(lq, kTileQueries) : 0u;
+      }
+    }
+    if (flags) atomicOr(&slot[2], flags);
+  }
+  __syncthreads();
+  const int plan_flags = slot[2];
+  uint32_t units = 0;
+  int ntiles = 0;
+  if (!(plan_flags & 1)) {
+    block_scan_excl(seg_tp, B, part);
+    ntiles = (int)seg_tp[B];
+    if (ntiles > p.max_tiles) {
+      ntiles = 0;  // cannot happen for valid tables: ceil-sum of tiles <= T/8 + B
+    }
+    for (int g = tid; g < ntiles; g += kScoreThreads) {
+      const int b = upper_bound_u32(seg_tp, B + 1, (uint32_t)g) - 1;
+      const int qb = p.cu_q[b], lq = p.cu_q[b + 1] - qb;
+      const int lk = min(p.cu_k[b + 1] - p.cu_k[b], p.Lmax);
+      const int off = p.offs ? p.offs[b] : 0;
+      const int ntile_b = (int)(seg_tp[b + 1] - seg_tp[b]);
+      const int i = ntile_b - 1 - (g - (int)seg_tp[b]);
+      const int nq_end = min((i + 1) * kTileQueries, lq);
+      const int nmax = clampi(off + nq_end, 0, lk);
+      unit_pf[g] = (uint32_t)ceil_div(nmax, chunk_keys);
+    }
+    __syncthreads();
+    block_scan_excl(unit_pf, ntiles, part);
+    units = unit_pf[ntiles];
+  }
+  if (tid == 0 && plan_flags) {
+    uint32_t st = 0;
+    if (plan_flags & 1) st |= kStatusBadSegments;
+    if (plan_flags & 2) st |= kStatusSeqlenBound;
+    atomicOr(p.ctrl + kCtrlStatus, st);
+  }
+
+  // ---- ticket loop ------------------------------------------------------------------------
+  if (tid == 0) slot[0] = (int)atomicAdd(p.ctrl + kCtrlTicket, 1u);
+  __syncthreads();
+  uint32_t u = (uint32_t)slot[0];
+  if (tid == 0 && u >= units + gridDim.x) atomicOr(p.ctrl + kCtrlStatus, kStatusCorruptCounter);
+
+  // lane roles (fixed for the whole kernel)
+  const int m = lane & 15;          // A row supplied by this lane / B column (key) supplied
+  const int e = lane >> 4;          // 8-dim chunk inside a 32-dim K-step
+  const int ga = m >> 2;            // accumulator group holding A row m
+  const int qa = 2 * wv + (ga >> 1);
+  const int ha = 32 * (ga & 1) + (m & 3);
+  const int go = lane >> 4;         // accumulator group of this lane
+  const int qo = 2 * wv + (go >> 1);
+  const int ho = 32 * (go & 1);
+
+  int iter = 0;
+  while (u < units) {
+    if (tid == 0) slot[4 + (iter & 1)] = (int)atomicAdd(p.ctrl + kCtrlTicket, 1u);
+
+    // decode u -> (tile g, chunk c) -> (segment b, tile i)
+    const int g = upper_bound_u32(unit_pf, ntiles + 1, u) - 1;
+    const int c = (int)(u - unit_pf[g]);
+    const int b = upper_bound_u32(seg_tp, B + 1, (uint32_t)g) - 1;
+    const int ntile_b = (int)(seg_tp[b + 1] - seg_tp[b]);
+    const int ti = ntile_b - 1 - (g - (int)seg_tp[b]);
+
+    const int qb = p.cu_q[b];
+    const int lq = p.cu_q[b + 1] - qb;
+    const int kb = p.cu_k[b];
+    const int lk = min(p.cu_k[b + 1] - kb, p.Lmax);
+    const int off = p.offs ? p.offs[b] : 0;
+    const int tq0 = ti * kTileQueries;
+    const int nq = min(kTileQueries, lq - tq0);
+    const int nmax = clampi(off + tq0 + nq, 0, lk);
+    const int kbeg = c * chunk_keys;
+    const int kend = min(kbeg + chunk_keys, nmax);
+
+    // A operand: this lane's row (query qa, head ha + 4*rb) for every row block and K-step.
+    bf16x8 qf[8][4];
+    if (qa < nq) {
+      const uint16_t* qrow = p.q + (int64_t)(qb + tq0 + qa) * (kHeads * kDim);
+#pragma unroll
+      for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          qf[rb][j] = *reinterpret_cast<const bf16x8*>(qrow + (ha + 4 * rb) * kDim + 32 * j + 8 * e);
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qf[rb][j] = bf16x8{};
+    }
+    // head weights of the heads this lane reduces: w[qo, ho .. ho+31]
+    float wr[32];
+    int n_o = 0;
+    if (qo < nq) {
+      const f32x4* wrow = reinterpret_cast<const f32x4*>(p.w + (int64_t)(qb + tq0 + qo) * kHeads + ho);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const f32x4 x = wrow[v];
+        wr[4 * v] = x[0];
+        wr[4 * v + 1] = x[1];
+        wr[4 * v + 2] = x[2];
+        wr[4 * v + 3] = x[3];
+      }
+      n_o = clampi(off + tq0 + qo + 1, 0, lk);
+    } else {
+#pragma unroll
+      for (int v = 0; v < 32; ++v) wr[v] = 0.f;
+    }
+    float* const orow = p.out + (int64_t)(qb + tq0 + min(qo, nq - 1)) * p.ld;
+    const bool storer = (go & 1) == 0;
+
+    // key tile staging: thread tid moves 16-byte chunks id = r*256 + tid (key id>>4, chunk id&15)
+    const uint16_t* const kseg = p.k + (int64_t)kb * kDim;
+    uint4 kreg[4];
+    auto gload = [&](int kt0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int id = r * kScoreThreads + tid;
+        const int s = id >> 4, cc = id & 15;
+        const int key = kt0 + s;
+        kreg[r] = key < lk ? *reinterpret_cast<const uint4*>(kseg + (int64_t)key * kDim + cc * 8)
+                           : make_uint4(0u, 0u, 0u, 0u);
+      }
+    };
+    auto swrite = [&](unsigned char* buf) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int id = r * kScoreThreads + tid;
+        const int s = id >> 4, cc = id & 15;
+        *reinterpret_cast<uint4*>(buf + s * (kDim * 2) + ((cc ^ (s & 15)) << 4)) = kreg[r];
+      }
+    };
+
+    const int ntl = kend > kbeg ? ceil_div(kend - kbeg, kTileKeys) : 0;
+    if (ntl > 0) {
+      gload(kbeg);
+      swrite(kbuf0);
+    }
+    __syncthreads();
+    for (int tt = 0; tt < ntl; ++tt) {
+      const unsigned char* cur = (tt & 1) ? kbuf1 : kbuf0;
+      unsigned char* nxt = (tt & 1) ? kbuf0 : kbuf1;
+      const bool more = tt + 1 < ntl;
+      const int kt0 = kbeg + tt * kTileKeys;
+      if (more) gload(kt0 + kTileKeys);
+#pragma unroll
+      for (int sb = 0; sb < kTileKeys / 16; ++sb) {
+        const int s = sb * 16 + m;
+        bf16x8 kf[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          kf[j] = *reinterpret_cast<const bf16x8*>(cur + s * (kDim * 2) + (((4 * j + e) ^ m) << 4));
+        f32x4 acc[8];
+#pragma unroll
+        for (int rb = 0; rb < 8; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int rb = 0; rb < 8; ++rb)
+            acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[rb][j], kf[j], acc[rb], 0, 0, 0);
+        // w * ReLU summed over this lane's 32 heads in ascending head order, then the other half.
+        float ps = 0.f;
+#pragma unroll
+        for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii)
+            ps = __builtin_fmaf(wr[4 * rb + ii], fmaxf(acc[rb][ii], 0.f), ps);
+        ps += __shfl_xor(ps, 16, 64);
+        const int key = kt0 + sb * 16 + m;
+        if (storer && key < n_o) orow[key] = ps;
+      }
+      if (more) swrite(nxt);
+      __syncthreads();
+    }
+    u = (uint32_t)slot[4 + (iter & 1)];
+    ++iter;
+  }
+
+  // ---- exit: the last block out resets the counters ----------------------------------------
+  if (tid == 0) {
+    __threadfence();
+    const uint32_t prev = atomicAdd(p.ctrl + kCtrlDone, 1u);
+    if (prev == gridDim.x - 1) {
+      const uint32_t tk = atomicAdd(p.ctrl + kCtrlTicket, 0u);
+      if (tk != units + gridDim.x) atomicOr(p.ctrl + kCtrlStatus, kStatusCorruptCounter);
+      atomicExch(p.ctrl + kCtrlTicket, 0u);
+      atomicExch(p.ctrl + kCtrlDone, 0u);
+    }
+  }
+}
+
+__global__ void ctrl_init_kernel(uint32_t* ctrl) {
+  if (threadIdx.x < kCtrlBytes / 4) ctrl[threadIdx.x] = 0u;
+}
+
+}  // namespace
+
+size_t score_smem_bytes(int B, int max_tiles) {
+  return (size_t)2 * kKBufBytes + kSlotInts * 4 + kPartEntries * 4 +
+         (size_t)((B + 1 + 3) & ~3) * 4 + (size_t)(max_tiles + 1) * 4;
+}
+
+size_t score_smem_limit() { return 80 * 1024; }
+
+hipError_t score_prepare(size_t max_smem) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_smem);
+}
+
+hipError_t score_occupancy(int* blocks_per_cu, size_t smem) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, score_kernel, kScoreThreads,
+                                                      smem);
+}
+
+hipError_t launch_score(const ScoreParams& p, int grid, size_t smem, hipStream_t s) {
+  hipLaunchKernelGGL(score_kernel, dim3(grid), dim3(kScoreThreads), smem, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_ctrl_init(uint32_t* ctrl, hipStream_t s) {
+  hipLaunchKernelGGL(ctrl_init_kernel, dim3(1), dim3(64), 0, s, ctrl);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,177 @@
+/*
+ * dsa_indexer.h — C ABI of the MI355X (gfx950) deterministic DSA indexer top-k scan.
+ *
+ * Operation (flashinfer PR #8691, "perf(cake_dsa_indexer_det): ticket scheduling on
+ * sm_107a, no fill kernel in eager entry", description): BF16 queries and keys, FP32 head
+ * weights and scores; for every query the scan returns the ids of its top-k keys; ids and
+ * scores do not depend on how the work is partitioned or chunked; equal scores go to the
+ * larger id.  The score itself is the lightning-indexer form (named by that page's
+ * vendoring note, formula not printed there and adopted here):
+ *
+ *     I[t, s] = sum_{h < H} w[t, h] * max(0, sum_{d < D} q[t, h, d] * k[s, d])
+ *
+ * Segments and causality (same page, eager-entry tables: single causal documents, context
+ * parallel tails, zigzag rank shares, split tails; causal query offsets of the eager entry):
+ * segment b holds queries cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and keys
+ * cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1.  Query t of segment b sits at position
+ * p = q_pos_offsets[b] + (t - cu_seqlens_q[b]) and sees the first
+ * n_t = min(max(p + 1, 0), len_k(b)) keys of its segment.
+ *
+ * Output row t: out_ids[t, 0 .. m-1] are the global key ids (row indices into k) of the
+ * top m = min(topk, n_t) keys under the order (score descending, id descending), written in
+ * ascending id order, out_scores[t, j] their FP32 scores (-0 is written as +0); slots
+ * m .. topk-1 hold id -1 and score -inf (-1 is the "no key" marker of the sparse-index
+ * consumer, flashinfer PR #4573 follow-ups).
+ *
+ * Determinism: every (t, s) score is computed by the same instruction sequence wherever
+ * and in whichever work unit it is computed, and the selection is a pure function of the
+ * row's scores, so outputs are bit-identical across runs, grid sizes, key chunkings,
+ * query splits and segment packings.
+ *
+ * Conventions common to every call:
+ *   - All data pointers are caller-owned DEVICE memory on the current HIP device.  The
+ *     library allocates nothing, frees nothing and never synchronises the stream.
+ *   - Tensors are dense row-major; q, k, w, out_* and workspace must be 16-byte aligned.
+ *   - Host-side arguments are validated; device-resident tables (cu_seqlens, offsets) are
+ *     validated by the kernel, which then skips the call's work and raises a status bit
+ *     in the workspace (read with dsa_indexer_read_status) instead of touching memory out
+ *     of bounds.
+ *   - Calls are asynchronous on `stream`.  A workspace must not be used by two calls that
+ *     can run concurrently.
+ *   - Return value: DSA_OK (0) or a negative DSA_ERR_* code; nothing is enqueued on error.
+ */
+#ifndef DSA_INDEXER_H_
+#define DSA_INDEXER_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define DSA_OK 0
+#define DSA_ERR_NULL (-1)       /* a required pointer is NULL                                  */
+#define DSA_ERR_ALIGN (-2)      /* a pointer is not 16-byte aligned                            */
+#define DSA_ERR_SHAPE (-3)      /* unsupported or inconsistent shape / topk                     */
+#define DSA_ERR_WORKSPACE (-4)  /* workspace_bytes below dsa_indexer_workspace_size()          */
+#define DSA_ERR_LAUNCH (-5)     /* a HIP launch failed; re-run dsa_indexer_workspace_init      */
+#define DSA_ERR_DEVICE (-6)     /* current device is not gfx950 or cannot be queried           */
+
+/* Device status bits, left in the workspace control block by the kernels. */
+#define DSA_STATUS_CORRUPT_COUNTER 0x1u /* work-unit counter was not zero at entry          */
+#define DSA_STATUS_BAD_SEGMENTS 0x2u    /* cu_seqlens not 0-based, non-decreasing, ending at T/Tkv */
+#define DSA_STATUS_SEQLEN_BOUND 0x4u    /* a segment has more keys than max_seqlen_k         */
+
+/* Supported sizes. */
+#define DSA_NUM_HEADS 64
+#define DSA_HEAD_DIM 128
+#define DSA_MAX_TOPK 2048
+#define DSA_MAX_SEQLEN_K 65536
+
+/* Host-side sizes; every field must be known without reading device memory. */
+typedef struct dsa_indexer_shape {
+  int32_t num_segments; /* B >= 1; cu_seqlens_* hold B+1 entries                              */
+  int32_t total_q;      /* T >= 0: rows of q, w, out_ids, out_scores                          */
+  int32_t total_k;      /* Tkv >= 0: rows of k                                                */
+  int32_t num_heads;    /* H, must be 64                                                      */
+  int32_t head_dim;     /* D, must be 128                                                     */
+  int32_t max_seqlen_k; /* upper bound on any segment's key count, 1..65536; 0 = min(Tkv,65536) */
+} dsa_indexer_shape;
+
+/*
+ * Bytes of workspace the top-k call needs for `shape`: a 256-byte control block (work-unit
+ * counter, exit counter, status word) followed by the FP32 score rows, T rows of
+ * round_up(max_seqlen_k, 64) floats.  Returns 0 if the shape is invalid.
+ */
+size_t dsa_indexer_workspace_size(const dsa_indexer_shape* shape);
+
+/*
+ * Zero the workspace control block, on `stream` (a small fill kernel, no memset, so the call
+ * can be captured in a graph).  Needed once per workspace before its first use, and again
+ * after any call that returned DSA_ERR_LAUNCH or left a status bit set.  Every completed call
+ * leaves the counters at zero again, so steady-state calls pay no reset.  Initialise and
+ * call on the same stream, or order the two streams (the page's stream-ordering note for
+ * prepared runners).
+ */
+int dsa_indexer_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The scan.  Enqueues the score kernel (persistent grid drawing work units from the
+ * self-resetting counter in the workspace) and the per-row top-k select kernel on `stream`.
+ *   q              bf16 [T, 64, 128]
+ *   k              bf16 [Tkv, 128]
+ *   w              fp32 [T, 64]
+ *   cu_seqlens_q   int32 [B+1], 0 = cu[0] <= ... <= cu[B] = T
+ *   cu_seqlens_k   int32 [B+1], 0 = cu[0] <= ... <= cu[B] = Tkv
+ *   q_pos_offsets  int32 [B] causal position of each segment's first query, or NULL (all 0)
+ *   topk           1 .. 2048
+ *   out_ids        int32 [T, topk]   (fully overwritten)
+ *   out_scores     fp32  [T, topk]   (fully overwritten)
+ *   workspace      >= dsa_indexer_workspace_size(shape) bytes, initialised once
+ */
+int dsa_indexer_topk(const dsa_indexer_shape* shape, const void* q, const void* k, const float* w,
+                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                     const int32_t* q_pos_offsets, int32_t topk, int32_t* out_ids,
+                     float* out_scores, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/*
+ * Score phase only ("indexer logits"): writes I[t, cu_seqlens_k[b] + j] to
+ * out_scores[t * ld_out + j] for every visible j < n_t and leaves every other element of
+ * out_scores untouched.  ld_out >= max_seqlen_k, multiple of 4.  The workspace needs only
+ * the 256-byte control block (and its init).
+ */
+int dsa_indexer_scores(const dsa_indexer_shape* shape, const void* q, const void* k,
+                       const float* w, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                       const int32_t* q_pos_offsets, float* out_scores, int64_t ld_out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Text of a DSA_ERR_* code. */
+const char* dsa_indexer_status_string(int code);
+
+/*
+ * Tuning knobs, for tests and measurement only; results never depend on them.
+ *   key_chunk_tiles  keys per work unit in tiles of 64 (0 = chosen from the shape)
+ *   grid_blocks      persistent score-kernel grid size (0 = CUs x resident blocks per CU)
+ */
+typedef struct dsa_indexer_tuning {
+  int32_t key_chunk_tiles;
+  int32_t grid_blocks;
+  int32_t reserved[6];
+} dsa_indexer_tuning;
+
+/*
+ * Per-kernel timing with HIP events recorded on the call's stream around each kernel.
+ * A profiler holds `capacity` call slots; dsa_indexer_profiler_read synchronises on the
+ * recorded events, returns the summed durations in milliseconds and the number of calls,
+ * and empties the slots.
+ */
+typedef struct dsa_indexer_profiler dsa_indexer_profiler;
+int dsa_indexer_profiler_create(int32_t capacity, dsa_indexer_profiler** out);
+int dsa_indexer_profiler_destroy(dsa_indexer_profiler* prof);
+int dsa_indexer_profiler_read(dsa_indexer_profiler* prof, double* score_ms, double* select_ms,
+                              int32_t* calls);
+
+/* dsa_indexer_topk with optional tuning (NULL = defaults) and optional profiler (NULL = none). */
+int dsa_indexer_topk_ex(const dsa_indexer_shape* shape, const void* q, const void* k,
+                        const float* w, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        const int32_t* q_pos_offsets, int32_t topk, int32_t* out_ids,
+                        float* out_scores, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream, const dsa_indexer_tuning* tuning,
+                        dsa_indexer_profiler* profiler);
+
+/*
+ * Test helper: synchronise `stream`, then copy the control block's status word and the two
+ * counters to the host.  Not for the hot path.
+ */
+int dsa_indexer_read_status(const void* workspace, hipStream_t stream, uint32_t* status,
+                            uint32_t* ticket, uint32_t* done);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_INDEXER_H_ */

@@ -1,0 +1,102 @@
+"""The C-ABI library loads, exports every declared symbol and validates arguments on the host.
+
+No compute call runs here: each call below is rejected by host-side checks
+before the library touches a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from deterministic_score_top_amd import indexer as ix
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa_indexer.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(dsa_indexer_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    L = ix.lib()
+    names = _declared()
+    assert set(names) == set(ix.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_workspace_size():
+    # control block + T rows of round_up(max_seqlen_k, 64) floats
+    assert ix.workspace_size(8192, 8192, 1, 8192) == 256 + 8192 * 8192 * 4
+    assert ix.workspace_size(4, 41986, 1, 41986) == 256 + 4 * 42048 * 4
+    assert ix.workspace_size(10, 100, 2, 0) == 256 + 10 * 128 * 4   # 0 -> Tkv
+    with pytest.raises(ix.DsaError):
+        ix.workspace_size(10, 100, 0, 0)
+    with pytest.raises(ix.DsaError):
+        ix.workspace_size(10, 100, 1, 70000)
+
+
+def test_status_strings():
+    L = ix.lib()
+    for code in range(0, -7, -1):
+        assert L.dsa_indexer_status_string(code)
+    assert L.dsa_indexer_status_string(-99) == b"unknown status"
+
+
+def _call(shape, ptrs, topk=16, ws_bytes=1 << 40):
+    L = ix.lib()
+    q, k, w, cq, ck, offs, oi, osc, ws = ptrs
+    V = ctypes.c_void_p
+    return L.dsa_indexer_topk(ctypes.byref(shape), V(q), V(k), V(w), V(cq), V(ck), V(offs), topk,
+                              V(oi), V(osc), V(ws), ws_bytes, None)
+
+
+GOOD = (0x10000, 0x20000, 0x30000, 0x40000, 0x50000, None, 0x60000, 0x70000, 0x80000)
+
+
+def _with(i, v):
+    p = list(GOOD)
+    p[i] = v
+    return tuple(p)
+
+
+def test_argument_errors():
+    s = ix.make_shape(16, 64, 1, 64)
+    assert _call(s, _with(0, None)) == -1          # q NULL
+    assert _call(s, _with(8, None)) == -1          # workspace NULL
+    assert _call(s, _with(1, 0x20008)) == -2       # k misaligned
+    assert _call(s, _with(3, 0x40002)) == -2       # cu_seqlens_q misaligned
+    assert _call(s, GOOD, topk=0) == -3
+    assert _call(s, GOOD, topk=2049) == -3
+    assert _call(s, GOOD, ws_bytes=100) == -4
+    bad = ix.make_shape(16, 64, 1, 64)
+    bad.num_heads = 32
+    assert _call(bad, GOOD) == -3
+    bad = ix.make_shape(16, 64, 1, 64)
+    bad.head_dim = 64
+    assert _call(bad, GOOD) == -3
+    bad = ix.make_shape(-1, 64, 1, 64)
+    assert _call(bad, GOOD) == -3
+    bad = ix.make_shape(16, 64, 0, 64)
+    assert _call(bad, GOOD) == -3
+
+
+def test_scores_argument_errors():
+    L = ix.lib()
+    s = ix.make_shape(16, 64, 1, 64)
+    V = ctypes.c_void_p
+    q, k, w, cq, ck, _, _, osc, ws = GOOD
+    assert L.dsa_indexer_scores(ctypes.byref(s), V(q), V(k), V(w), V(cq), V(ck), None, V(osc), 60, V(ws),
+                                1 << 20, None) == -3                       # ld below max_seqlen_k
+    assert L.dsa_indexer_scores(ctypes.byref(s), V(q), V(k), V(w), V(cq), V(ck), None, V(osc), 64, V(ws),
+                                16, None) == -4                            # no room for the control block
+
+
+def test_profiler_argument_errors():
+    L = ix.lib()
+    h = ctypes.c_void_p()
+    assert L.dsa_indexer_profiler_create(0, ctypes.byref(h)) == -3
+    assert L.dsa_indexer_profiler_read(None, None, None, None) == -1

@@ -1,0 +1,222 @@
+"""GPU parity of the HIP path (through the C ABI) against the FP64 oracle.
+
+Sizes: the small cases span several 8-query tiles and 64-key tiles with ragged
+tails; the full configurations are checked on sampled rows against the oracle
+and on every row through properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+from deterministic_score_top_amd import indexer as ix
+from deterministic_score_top_amd import workloads as W
+from oracle import dsa_oracle as O
+from tests.parity import check_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(wl):
+    d = "cuda"
+    offs = None if wl.q_pos_offsets is None else wl.q_pos_offsets.to(d)
+    return (wl.q.to(d), wl.k.to(d), wl.w.to(d), wl.cu_seqlens_q.to(d), wl.cu_seqlens_k.to(d), offs)
+
+
+def _run(wl, dev_args=None, **kw):
+    q, k, w, cq, ck, offs = dev_args or _dev(wl)
+    ids, sc = ix.topk(q, k, w, cq, ck, offs, topk=wl.topk, max_seqlen_k=wl.max_seqlen_k, **kw)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), sc.cpu().numpy()
+
+
+def _oracle(wl, rows=None):
+    return O.topk_workload(wl, rows)
+
+
+def _check_all(wl, exact=False, **kw):
+    ids, sc = _run(wl, **kw)
+    oi, osc, det = _oracle(wl)
+    check_rows(ids, sc, range(wl.T), oi, osc, det, wl.topk, exact=exact)
+    return ids, sc
+
+
+def _structural(wl, ids, sc):
+    """Properties of every row at any size: count, range, order, padding, finite scores."""
+    cu_q, cu_k = wl.cu_seqlens_q.numpy(), wl.cu_seqlens_k.numpy()
+    offs = None if wl.q_pos_offsets is None else wl.q_pos_offsets.numpy()
+    for t in range(wl.T):
+        first, n = O.visible(cu_q, cu_k, offs, t)
+        m = min(n, wl.topk)
+        row = ids[t]
+        assert np.all(row[m:] == -1) and np.all(np.isneginf(sc[t, m:])), t
+        assert np.all(np.diff(row[:m]) > 0), t
+        assert m == 0 or (row[0] >= first and row[m - 1] < first + n), t
+        assert np.all(np.isfinite(sc[t, :m])), t
+
+
+def test_causal_n1024_all_rows():
+    _check_all(W.make("causal_n1024"))
+
+
+RAGGED = [
+    # q_lens, k_lens, offsets, topk
+    ([13, 0, 29, 5, 1], [70, 3, 130, 0, 200], [0, 2, 100, 1, 500], 16),
+    ([64, 9], [64, 300], [0, 250], 1),
+    ([17, 33], [100, 129], None, 2048),
+    ([40], [257], [200], 64),
+    ([0, 0, 7], [5, 0, 9], [0, 0, 0], 3),
+]
+
+
+@pytest.mark.parametrize("case", range(len(RAGGED)))
+def test_ragged_segments(case):
+    ql, kl, offs, topk = RAGGED[case]
+    _check_all(W.random_segments(ql, kl, offs, topk, seed=case))
+
+
+@pytest.mark.parametrize("distinct", [None, 16, 2])
+def test_integer_inputs_exact(distinct):
+    wl = W.integer_valued([37, 20], [300, 129], [100, 5], topk=40, seed=3, distinct_keys=distinct)
+    _check_all(wl, exact=True)
+
+
+def test_scores_export():
+    wl = W.random_segments([21, 11], [90, 140], [40, 0], topk=8, seed=5)
+    q, k, w, cq, ck, offs = _dev(wl)
+    out = ix.scores(q, k, w, cq, ck, offs, max_seqlen_k=wl.max_seqlen_k).cpu().numpy()
+    _, _, det = _oracle(wl)
+    for t in range(wl.T):
+        first, s_all = det[t]
+        n = len(s_all)
+        tau = 1e-4 * max(1e-30, float(np.max(np.abs(s_all)))) if n else 0.0
+        assert np.all(np.abs(out[t, :n] - s_all) <= tau), t
+        assert np.all(np.isnan(out[t, n:])), t
+
+
+def test_run_to_run_bitwise():
+    wl = W.make("causal_n1024", seed=1)
+    dev = _dev(wl)
+    a = _run(wl, dev)
+    for _ in range(3):
+        b = _run(wl, dev)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+@pytest.mark.parametrize("tuning", [dict(key_chunk_tiles=1), dict(key_chunk_tiles=3),
+                                    dict(key_chunk_tiles=16, grid_blocks=1),
+                                    dict(key_chunk_tiles=2, grid_blocks=7), dict(grid_blocks=1000)])
+def test_chunking_and_grid_bitwise(tuning):
+    wl = W.random_segments([300, 77], [700, 1500], [400, 1000], topk=128, seed=8)
+    dev = _dev(wl)
+    a = _run(wl, dev)
+    b = _run(wl, dev, tuning=tuning)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+def test_query_split_bitwise():
+    wl = W.random_segments([200], [260], [60], topk=64, seed=9)
+    full = _run(wl)
+    parts = []
+    for lo, hi in ((0, 77), (77, 200)):
+        sub = W.Workload("part", wl.q[lo:hi].contiguous(), wl.k, wl.w[lo:hi].contiguous(),
+                         torch.tensor([0, hi - lo], dtype=torch.int32), wl.cu_seqlens_k,
+                         torch.tensor([60 + lo], dtype=torch.int32), 64, 260)
+        parts.append(_run(sub))
+    ids = np.concatenate([p[0] for p in parts])
+    sc = np.concatenate([p[1] for p in parts])
+    assert np.array_equal(full[0], ids) and np.array_equal(full[1].view(np.uint32), sc.view(np.uint32))
+
+
+def test_segment_packing_bitwise():
+    wl = W.random_segments([45, 60], [300, 90], [255, 0], topk=32, seed=10)
+    packed = _run(wl)
+    a = W.Workload("a", wl.q[:45].contiguous(), wl.k[:300].contiguous(), wl.w[:45].contiguous(),
+                   torch.tensor([0, 45], dtype=torch.int32), torch.tensor([0, 300], dtype=torch.int32),
+                   torch.tensor([255], dtype=torch.int32), 32, 300)
+    b = W.Workload("b", wl.q[45:].contiguous(), wl.k[300:].contiguous(), wl.w[45:].contiguous(),
+                   torch.tensor([0, 60], dtype=torch.int32), torch.tensor([0, 90], dtype=torch.int32),
+                   torch.tensor([0], dtype=torch.int32), 32, 300)
+    ra, rb = _run(a), _run(b)
+    ids_b = np.where(rb[0] >= 0, rb[0] + 300, -1)
+    assert np.array_equal(packed[0], np.concatenate([ra[0], ids_b]))
+    assert np.array_equal(packed[1].view(np.uint32), np.concatenate([ra[1], rb[1]]).view(np.uint32))
+
+
+def test_tail_rows_equal_full_causal_rows():
+    full = W.single_causal(4096, 512, seed=4)
+    rf = _run(full)
+    tail = W.Workload("tail", full.q[3072:].contiguous(), full.k, full.w[3072:].contiguous(),
+                      torch.tensor([0, 1024], dtype=torch.int32), full.cu_seqlens_k,
+                      torch.tensor([3072], dtype=torch.int32), 512, 4096)
+    rt = _run(tail)
+    assert np.array_equal(rf[0][3072:], rt[0])
+    assert np.array_equal(rf[1][3072:].view(np.uint32), rt[1].view(np.uint32))
+
+
+def test_control_block_left_clean():
+    wl = W.random_segments([50, 30], [400, 100], [300, 0], topk=64, seed=11)
+    q, k, w, cq, ck, offs = _dev(wl)
+    ws = ix.alloc_workspace(wl.T, wl.Tkv, wl.B, wl.max_seqlen_k)
+    for _ in range(3):
+        ix.topk(q, k, w, cq, ck, offs, topk=64, workspace=ws, max_seqlen_k=wl.max_seqlen_k)
+        assert ix.read_status(ws) == (0, 0, 0)
+
+
+def test_poisoned_counter_flagged_then_recovered():
+    wl = W.random_segments([50, 30], [400, 100], [300, 0], topk=64, seed=12)
+    q, k, w, cq, ck, offs = _dev(wl)
+    ws = ix.alloc_workspace(wl.T, wl.Tkv, wl.B, wl.max_seqlen_k)
+    good = _run(wl, (q, k, w, cq, ck, offs), workspace=ws)
+    ws[0:4].view(torch.int32).fill_(123456)   # stale ticket word
+    ix.topk(q, k, w, cq, ck, offs, topk=64, workspace=ws, max_seqlen_k=wl.max_seqlen_k)
+    st, tk, dn = ix.read_status(ws)
+    assert st & ix.STATUS_CORRUPT_COUNTER and tk == 0 and dn == 0
+    ix.workspace_init(ws)
+    again = _run(wl, (q, k, w, cq, ck, offs), workspace=ws)
+    assert ix.read_status(ws) == (0, 0, 0)
+    assert np.array_equal(good[0], again[0]) and np.array_equal(good[1], again[1])
+
+
+def test_bad_segment_table_is_flagged():
+    wl = W.random_segments([20, 12], [100, 50], [0, 0], topk=8, seed=13)
+    q, k, w, cq, ck, offs = _dev(wl)
+    cq_bad = torch.tensor([0, 20, 31], dtype=torch.int32, device="cuda")  # does not end at T=32
+    ws = ix.alloc_workspace(wl.T, wl.Tkv, wl.B, wl.max_seqlen_k)
+    ids, sc = ix.topk(q, k, w, cq_bad, ck, offs, topk=8, workspace=ws, max_seqlen_k=wl.max_seqlen_k)
+    st, tk, dn = ix.read_status(ws)
+    assert st & ix.STATUS_BAD_SEGMENTS and tk == 0 and dn == 0
+    assert bool((ids == -1).all())
+
+
+FULL = ["causal_n8192", "cp_tail", "zigzag16", "zigzag8", "split_tail", "split_tail_tie", "causal_n16384"]
+
+
+def _sample_rows(wl, nsamp=12, seed=0):
+    T = wl.T
+    rng = np.random.default_rng(seed)
+    rows = {0, T - 1, min(T - 1, wl.topk - 1), min(T - 1, wl.topk), T // 2}
+    rows |= set(rng.integers(0, T, size=nsamp).tolist())
+    cu = wl.cu_seqlens_q.numpy()
+    for b in range(len(cu) - 1):        # first and last query of a few segments
+        if cu[b + 1] > cu[b] and b % 7 == 0:
+            rows |= {int(cu[b]), int(cu[b + 1] - 1)}
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_config_sampled(name):
+    wl = W.make(name)
+    ids, sc = _run(wl)
+    _structural(wl, ids, sc)
+    rows = _sample_rows(wl)
+    oi, osc, det = _oracle(wl, rows)
+    check_rows(ids, sc, rows, oi, osc, det, wl.topk)
+    if name == "split_tail_tie":
+        # identical key rows must score identically wherever they sit
+        kb = wl.k.view(torch.int16).numpy()
+        for t in range(wl.T):
+            groups = {}
+            for i, s in zip(ids[t], sc[t]):
+                if i >= 0:
+                    groups.setdefault(kb[i].tobytes(), set()).add(float(s))
+            assert all(len(v) == 1 for v in groups.values())
