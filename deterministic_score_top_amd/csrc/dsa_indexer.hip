@@ -104,12 +104,13 @@ int launch_scores(const Call& c, hipStream_t stream) {
     chunk = c.tuning->key_chunk_tiles;
   }
   if (chunk == 0) {
-    // about four units per resident block, chunks of at most 16 key tiles (1024 keys)
+    // Units should be few (each start reloads the query block) but numerous enough to balance:
+    // about two per resident block, from an upper bound of the work in 64-key tiles.
     const int64_t key_tiles = (L + dsa::kTileKeys - 1) / dsa::kTileKeys;
     const int64_t work = (int64_t)max_tiles * key_tiles;
-    int64_t ct = work / (4 * (int64_t)grid_default);
+    int64_t ct = work / (2 * (int64_t)grid_default);
     if (ct < 1) ct = 1;
-    if (ct > 16) ct = 16;
+    if (ct > key_tiles) ct = key_tiles;
     chunk = (int)ct;
   }
   if ((int64_t)chunk * dsa::kTileKeys > (int64_t)1 << 30) return DSA_ERR_SHAPE;
@@ -278,7 +279,7 @@ int dsa_indexer_profiler_create(int32_t capacity, dsa_indexer_profiler** out) {
 int dsa_indexer_profiler_destroy(dsa_indexer_profiler* prof) {
   if (!prof) return DSA_ERR_NULL;
   for (auto& e : prof->ev)
-    if (e) hipEventDestroy(e);
+    if (e) (void)hipEventDestroy(e);
   delete prof;
   return DSA_OK;
 }

@@ -9,10 +9,12 @@ namespace dsa {
 
 constexpr int kHeads = 64;       // indexer heads H
 constexpr int kDim = 128;        // head dim D
-constexpr int kScoreThreads = 256;
+#ifndef DSA_SCORE_THREADS
+#define DSA_SCORE_THREADS 512
+#endif
+constexpr int kScoreThreads = DSA_SCORE_THREADS;  // one query per wave
 constexpr int kWaves = kScoreThreads / 64;
-constexpr int kQueriesPerWave = 2;
-constexpr int kTileQueries = kWaves * kQueriesPerWave;  // queries per work unit (8)
+constexpr int kTileQueries = kWaves;                     // one query per wave; queries per unit
 constexpr int kTileKeys = 64;                            // keys per LDS stage
 constexpr int kCtrlBytes = 256;                          // control block at workspace offset 0
 constexpr int kMaxTopk = 2048;

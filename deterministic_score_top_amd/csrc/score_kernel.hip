@@ -13,19 +13,22 @@
 // tile (most visible keys) to the first, so the cheapest units run last.  The last block to
 // leave resets the counter, so steady-state calls pay no reset.
 //
-// Inside a unit (256 threads, 4 waves, 2 queries per wave):
-//   * each wave holds the BF16 A operand of its 2 queries x 64 heads x 128 dims in VGPRs
-//     (8 row blocks of 16 rows x 4 K-steps of 32), loaded once per unit;
+// Inside a unit (512 threads = 8 waves, one query per wave):
+//   * each wave holds the BF16 A operand of its query (64 heads x 128 dims: 2 row blocks of
+//     32 rows x 8 K-steps of 16) in VGPRs, loaded once per unit, and the query's head weights;
 //   * 64-key tiles of k are staged in LDS (double buffered, 16-byte chunks XOR-swizzled by
 //     key so the B-operand reads and the tile writes are bank-conflict free);
-//   * per 16-key column block: 32 v_mfma_f32_16x16x32_bf16 (FP32 accumulate, d ascending);
-//   * epilogue in registers: lane (group G = lane/16) holds heads 32*(G&1) + 0..31 of query
-//     G>>1 for key lane&15; it sums w*ReLU over its 32 heads in ascending head order with
-//     FMA, then adds the other half from lane^16.  The instruction sequence per (t, s) is the
-//     same in every unit, tile position and chunking, so scores are bit-reproducible.
+//   * per tile: 2 column blocks of 32 keys x 2 row blocks x 8 K-steps of
+//     v_mfma_f32_32x32x16_bf16 (FP32 accumulate, d ascending);
+//   * epilogue in registers: lane half hf holds heads 32*rb + 16*hf + i (i = 0..15) of key
+//     lane&31; it sums w * ReLU over them in a fixed order (ReLU as one integer max on the
+//     float bits), then adds the other half's sum with v_permlane32_swap.  The instruction
+//     sequence per (t, s) is the same in every unit, tile position, chunking and grid, so
+//     every score is bit-reproducible.
 //
-// Row mapping of the A operand (row m of row block rb, held in the accumulators by lane
-// group m/4): query (m/4)>>1, head 32*((m/4)&1) + 4*rb + (m&3).
+// Row mapping of the A operand: row n of row block rb carries head
+// 32*rb + 16*((n>>2)&1) + 4*(n>>3) + (n&3), which puts heads 32*rb + 16*hf + 0..15 in the
+// accumulator registers 0..15 of lane half hf.
 
 #include "dsa_internal.h"
 
@@ -34,12 +37,23 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kKBufBytes = kTileKeys * kDim * 2;  // one staged key tile: 16 KiB
 constexpr int kSlotInts = 16;
 constexpr int kPartEntries = kScoreThreads + 4;
+constexpr int kStageChunks = kTileKeys * kDim * 2 / 16 / kScoreThreads;  // 16-byte chunks per thread per tile
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// max(x, +0) for finite x, as one integer max on the bits (-0 and negatives map to +0).
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// x[l] + x[l ^ 32], lower half first in every lane (v_permlane32_swap, no LDS traffic).
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
 
 // First index in arr[0..n) whose value exceeds x (arr non-decreasing).
@@ -63,20 +77,26 @@ __device__ void block_scan_excl(uint32_t* arr, int n, uint32_t* part) {
   part[tid] = s;
   __syncthreads();
   if (tid < 64) {
-    const uint32_t a0 = part[4 * tid], a1 = part[4 * tid + 1], a2 = part[4 * tid + 2],
-                   a3 = part[4 * tid + 3];
-    const uint32_t sum = a0 + a1 + a2 + a3;
+    constexpr int kPer = kScoreThreads / 64;  // partial sums per lane
+    uint32_t a[kPer];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      a[i] = part[kPer * tid + i];
+      sum += a[i];
+    }
     uint32_t inc = sum;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const uint32_t y = __shfl_up(inc, o, 64);
       if (tid >= o) inc += y;
     }
-    const uint32_t ex = inc - sum;
-    part[4 * tid] = ex;
-    part[4 * tid + 1] = ex + a0;
-    part[4 * tid + 2] = ex + a0 + a1;
-    part[4 * tid + 3] = ex + a0 + a1 + a2;
+    uint32_t ex = inc - sum;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      part[kPer * tid + i] = ex;
+      ex += a[i];
+    }
     if (tid == 63) part[kScoreThreads] = inc;
   }
   __syncthreads();
@@ -161,15 +181,12 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
   uint32_t u = (uint32_t)slot[0];
   if (tid == 0 && u >= units + gridDim.x) atomicOr(p.ctrl + kCtrlStatus, kStatusCorruptCounter);
 
-  // lane roles (fixed for the whole kernel)
-  const int m = lane & 15;          // A row supplied by this lane / B column (key) supplied
-  const int e = lane >> 4;          // 8-dim chunk inside a 32-dim K-step
-  const int ga = m >> 2;            // accumulator group holding A row m
-  const int qa = 2 * wv + (ga >> 1);
-  const int ha = 32 * (ga & 1) + (m & 3);
-  const int go = lane >> 4;         // accumulator group of this lane
-  const int qo = 2 * wv + (go >> 1);
-  const int ho = 32 * (go & 1);
+  // lane roles (fixed for the whole kernel): one query per wave; A row / B column n, lane half hf
+  const int n = lane & 31;
+  const int hf = lane >> 5;
+  // head held in A row n of row block rb: 32*rb + 16*((n>>2)&1) + 4*(n>>3) + (n&3), so that the
+  // accumulator register i of row block rb in lane half hf holds head 32*rb + 16*hf + i
+  const int ha = 16 * ((n >> 2) & 1) + 4 * (n >> 3) + (n & 3);
 
   int iter = 0;
   while (u < units) {
@@ -193,103 +210,110 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
     const int kbeg = c * chunk_keys;
     const int kend = min(kbeg + chunk_keys, nmax);
 
-    // A operand: this lane's row (query qa, head ha + 4*rb) for every row block and K-step.
-    bf16x8 qf[8][4];
-    if (qa < nq) {
-      const uint16_t* qrow = p.q + (int64_t)(qb + tq0 + qa) * (kHeads * kDim);
-#pragma unroll
-      for (int rb = 0; rb < 8; ++rb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          qf[rb][j] = *reinterpret_cast<const bf16x8*>(qrow + (ha + 4 * rb) * kDim + 32 * j + 8 * e);
-    } else {
-#pragma unroll
-      for (int rb = 0; rb < 8; ++rb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) qf[rb][j] = bf16x8{};
-    }
-    // head weights of the heads this lane reduces: w[qo, ho .. ho+31]
+    // this wave's query (tile-local index wv): A operand for both row blocks and all 8 K-steps
+    const bool qvalid = wv < nq;
+    bf16x8 qf[2][8];
     float wr[32];
     int n_o = 0;
-    if (qo < nq) {
-      const f32x4* wrow = reinterpret_cast<const f32x4*>(p.w + (int64_t)(qb + tq0 + qo) * kHeads + ho);
+    if (qvalid) {
+      const int64_t t = qb + tq0 + wv;
+      const uint16_t* qrow = p.q + t * (kHeads * kDim);
 #pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const f32x4 x = wrow[v];
-        wr[4 * v] = x[0];
-        wr[4 * v + 1] = x[1];
-        wr[4 * v + 2] = x[2];
-        wr[4 * v + 3] = x[3];
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          qf[rb][j] = *reinterpret_cast<const bf16x8*>(qrow + (32 * rb + ha) * kDim + 16 * j + 8 * hf);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const f32x4* wrow = reinterpret_cast<const f32x4*>(p.w + t * kHeads + 32 * rb + 16 * hf);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const f32x4 x = wrow[v];
+          wr[16 * rb + 4 * v] = x[0];
+          wr[16 * rb + 4 * v + 1] = x[1];
+          wr[16 * rb + 4 * v + 2] = x[2];
+          wr[16 * rb + 4 * v + 3] = x[3];
+        }
       }
-      n_o = clampi(off + tq0 + qo + 1, 0, lk);
+      n_o = clampi(off + tq0 + wv + 1, 0, lk);
     } else {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qf[rb][j] = bf16x8{};
 #pragma unroll
       for (int v = 0; v < 32; ++v) wr[v] = 0.f;
     }
-    float* const orow = p.out + (int64_t)(qb + tq0 + min(qo, nq - 1)) * p.ld;
-    const bool storer = (go & 1) == 0;
+    float* const orow = p.out + (int64_t)(qb + tq0 + min(wv, nq - 1)) * p.ld;
 
-    // key tile staging: thread tid moves 16-byte chunks id = r*256 + tid (key id>>4, chunk id&15)
+    // key tile staging: thread tid moves 16-byte chunks id = r*kScoreThreads + tid; tiles are
+    // fetched two ahead of the one being multiplied (two register stages, two LDS buffers)
     const uint16_t* const kseg = p.k + (int64_t)kb * kDim;
-    uint4 kreg[4];
-    auto gload = [&](int kt0) {
+    uint4 kregA[kStageChunks], kregB[kStageChunks];
+    auto gload = [&](uint4 (&kr)[kStageChunks], int kt0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < kStageChunks; ++r) {
         const int id = r * kScoreThreads + tid;
         const int s = id >> 4, cc = id & 15;
         const int key = kt0 + s;
-        kreg[r] = key < lk ? *reinterpret_cast<const uint4*>(kseg + (int64_t)key * kDim + cc * 8)
-                           : make_uint4(0u, 0u, 0u, 0u);
+        kr[r] = key < lk ? *reinterpret_cast<const uint4*>(kseg + (int64_t)key * kDim + cc * 8)
+                         : make_uint4(0u, 0u, 0u, 0u);
       }
     };
-    auto swrite = [&](unsigned char* buf) {
+    auto swrite = [&](const uint4 (&kr)[kStageChunks], unsigned char* buf) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < kStageChunks; ++r) {
         const int id = r * kScoreThreads + tid;
         const int s = id >> 4, cc = id & 15;
-        *reinterpret_cast<uint4*>(buf + s * (kDim * 2) + ((cc ^ (s & 15)) << 4)) = kreg[r];
+        *reinterpret_cast<uint4*>(buf + s * (kDim * 2) + ((cc ^ (s & 15)) << 4)) = kr[r];
+      }
+    };
+    // one 64-key tile: per column block of 32 keys, 2 row blocks x 8 K-steps of MFMA, then the
+    // epilogue (the first block's epilogue can run under the second block's MFMAs)
+    auto compute = [&](const unsigned char* cur, int kt0) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+        const int s = 32 * cb + n;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const bf16x8 kf =
+              *reinterpret_cast<const bf16x8*>(cur + s * (kDim * 2) + (((2 * j + hf) ^ (n & 15)) << 4));
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][j], kf, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][j], kf, acc1, 0, 0, 0);
+        }
+        // w * ReLU over this lane's 32 heads (two ascending runs of 16), then the other lane
+        // half's 32 heads.  ReLU is an integer max on the float bits: negative values and -0
+        // are negative as int32 and become +0; non-negative values pass unchanged.
+        float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          p0 = __builtin_fmaf(wr[i], relu_bits(acc0[i]), p0);
+          p1 = __builtin_fmaf(wr[16 + i], relu_bits(acc1[i]), p1);
+        }
+        const float score = half_swap_sum(p0 + p1);
+        const int key = kt0 + 32 * cb + n;
+        if (hf == 0 && key < n_o) orow[key] = score;
       }
     };
 
     const int ntl = kend > kbeg ? ceil_div(kend - kbeg, kTileKeys) : 0;
-    if (ntl > 0) {
-      gload(kbeg);
-      swrite(kbuf0);
-    }
+    if (ntl > 0) gload(kregA, kbeg);
+    if (ntl > 1) gload(kregB, kbeg + kTileKeys);
+    if (ntl > 0) swrite(kregA, kbuf0);
     __syncthreads();
-    for (int tt = 0; tt < ntl; ++tt) {
-      const unsigned char* cur = (tt & 1) ? kbuf1 : kbuf0;
-      unsigned char* nxt = (tt & 1) ? kbuf0 : kbuf1;
-      const bool more = tt + 1 < ntl;
+    for (int tt = 0; tt < ntl; tt += 2) {
       const int kt0 = kbeg + tt * kTileKeys;
-      if (more) gload(kt0 + kTileKeys);
-#pragma unroll
-      for (int sb = 0; sb < kTileKeys / 16; ++sb) {
-        const int s = sb * 16 + m;
-        bf16x8 kf[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          kf[j] = *reinterpret_cast<const bf16x8*>(cur + s * (kDim * 2) + (((4 * j + e) ^ m) << 4));
-        f32x4 acc[8];
-#pragma unroll
-        for (int rb = 0; rb < 8; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int rb = 0; rb < 8; ++rb)
-            acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[rb][j], kf[j], acc[rb], 0, 0, 0);
-        // w * ReLU summed over this lane's 32 heads in ascending head order, then the other half.
-        float ps = 0.f;
-#pragma unroll
-        for (int rb = 0; rb < 8; ++rb)
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii)
-            ps = __builtin_fmaf(wr[4 * rb + ii], fmaxf(acc[rb][ii], 0.f), ps);
-        ps += __shfl_xor(ps, 16, 64);
-        const int key = kt0 + sb * 16 + m;
-        if (storer && key < n_o) orow[key] = ps;
-      }
-      if (more) swrite(nxt);
+      // tile tt is in kbuf0, tile tt+1 is in flight in kregB, kregA is free
+      if (tt + 2 < ntl) gload(kregA, kt0 + 2 * kTileKeys);
+      compute(kbuf0, kt0);
+      if (tt + 1 < ntl) swrite(kregB, kbuf1);
+      __syncthreads();
+      if (tt + 1 >= ntl) break;
+      // tile tt+1 is in kbuf1, tile tt+2 is in flight in kregA, kregB is free
+      if (tt + 3 < ntl) gload(kregB, kt0 + 3 * kTileKeys);
+      compute(kbuf1, kt0 + kTileKeys);
+      if (tt + 2 < ntl) swrite(kregA, kbuf0);
       __syncthreads();
     }
     u = (uint32_t)slot[4 + (iter & 1)];
