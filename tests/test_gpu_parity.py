@@ -80,6 +80,15 @@ def test_integer_inputs_exact(distinct):
     _check_all(wl, exact=True)
 
 
+@pytest.mark.parametrize("distinct,nk,topk", [(2, 6000, 700), (16, 3000, 333), (None, 20000, 2048), (1, 9000, 2048)])
+def test_select_long_rows_exact(distinct, nk, topk):
+    # long rows of exact scores: few distinct values force the select kernel's overflow path
+    # (the threshold bin holds more keys than a wave's copy region); distinct=None is the
+    # ordinary path on a long row
+    wl = W.integer_valued([6], [nk], [nk - 6], topk=topk, seed=nk, distinct_keys=distinct)
+    _check_all(wl, exact=True)
+
+
 def test_scores_export():
     wl = W.random_segments([21, 11], [90, 140], [40, 0], topk=8, seed=5)
     q, k, w, cq, ck, offs = _dev(wl)
