@@ -30,9 +30,11 @@ flashinfer PR #4573, "feat(cake_sparse_mla): support SM100 and SM103"):
   sparse-index consumption), and score -inf.
 * Output order within a row: ascending id.
 
-Readings where the pages are silent are listed in the design notes of the
-repository (formula, inclusive diagonal, per-segment offsets, global ids,
-ascending order, -inf padding score).
+Readings where the pages are silent: the formula above with no extra scale;
+an inclusive causal diagonal with positions past a segment's end seeing the
+whole segment; one causal offset per segment (absent = 0); ids are global
+row indices of k; each row lists its ids in ascending order; padding slots
+hold id -1 and score -inf; -0 and +0 are the same score.
 
 Everything here is FP64: BF16 and FP32 inputs convert to FP64 exactly, the
 dot products use a library matmul, the head reduction a library
