@@ -42,6 +42,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kKBufBytes = kTileKeys * kDim * 2;  // one staged key tile: 16 KiB
 constexpr int kSlotInts = 16;
 constexpr int kPartEntries = kScoreThreads + 4;
+// Buffer resource word 3 for raw (stride 0) 32-bit buffers on gfx9-family parts, and a byte
+// offset that is always out of range (dropped store).
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kDropOffset = 0x40000000;
 constexpr int kStageChunks = kTileKeys * kDim * 2 / 16 / kScoreThreads;  // 16-byte chunks per thread per tile
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -121,7 +125,9 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  // wave index, explicitly wave-uniform so per-wave values (query row, buffer resources) live
+  // in scalar registers
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int B = p.B;
   const int chunk_keys = p.chunk_tiles * kTileKeys;
 
@@ -193,11 +199,13 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
     if (tid == 0) slot[4 + (iter & 1)] = (int)atomicAdd(p.ctrl + kCtrlTicket, 1u);
 
     // decode u -> (tile g, chunk c) -> (segment b, tile i)
-    const int g = upper_bound_u32(unit_pf, ntiles + 1, u) - 1;
-    const int c = (int)(u - unit_pf[g]);
-    const int b = upper_bound_u32(seg_tp, B + 1, (uint32_t)g) - 1;
-    const int ntile_b = (int)(seg_tp[b + 1] - seg_tp[b]);
-    const int ti = ntile_b - 1 - (g - (int)seg_tp[b]);
+    // (every lane computes the same values; readfirstlane makes that visible to the compiler so
+    // the unit's scalars and buffer resources stay in scalar registers)
+    const int g = __builtin_amdgcn_readfirstlane(upper_bound_u32(unit_pf, ntiles + 1, u) - 1);
+    const int c = __builtin_amdgcn_readfirstlane((int)(u - unit_pf[g]));
+    const int b = __builtin_amdgcn_readfirstlane(upper_bound_u32(seg_tp, B + 1, (uint32_t)g) - 1);
+    const int ntile_b = __builtin_amdgcn_readfirstlane((int)(seg_tp[b + 1] - seg_tp[b]));
+    const int ti = ntile_b - 1 - (g - __builtin_amdgcn_readfirstlane((int)seg_tp[b]));
 
     const int qb = p.cu_q[b];
     const int lq = p.cu_q[b + 1] - qb;
@@ -245,19 +253,24 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
       for (int v = 0; v < 32; ++v) wr[v] = 0.f;
     }
     float* const orow = p.out + (int64_t)(qb + tq0 + min(wv, nq - 1)) * p.ld;
+    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(orow, (short)0, n_o * 4, kRsrcWord3);
 
     // key tile staging: thread tid moves 16-byte chunks id = r*kScoreThreads + tid; tiles are
     // fetched two ahead of the one being multiplied (two register stages, two LDS buffers)
-    const uint16_t* const kseg = p.k + (int64_t)kb * kDim;
+    // Raw buffer resources with hardware range checks: keys at or past the segment's end read
+    // as zero, and score stores past the query's visible count (or from lane half 1, which
+    // holds the same sums) are dropped.  The tile loop therefore has no branches around memory
+    // operations.
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(p.k + (int64_t)kb * kDim), (short)0, lk * (kDim * 2), kRsrcWord3);
     uint4 kregA[kStageChunks], kregB[kStageChunks];
     auto gload = [&](uint4 (&kr)[kStageChunks], int kt0) {
 #pragma unroll
       for (int r = 0; r < kStageChunks; ++r) {
         const int id = r * kScoreThreads + tid;
         const int s = id >> 4, cc = id & 15;
-        const int key = kt0 + s;
-        kr[r] = key < lk ? *reinterpret_cast<const uint4*>(kseg + (int64_t)key * kDim + cc * 8)
-                         : make_uint4(0u, 0u, 0u, 0u);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(krs, (kt0 + s) * (kDim * 2) + cc * 16, 0, 0);
+        kr[r] = make_uint4(v[0], v[1], v[2], v[3]);
       }
     };
     auto swrite = [&](const uint4 (&kr)[kStageChunks], unsigned char* buf) {
@@ -268,53 +281,88 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
         *reinterpret_cast<uint4*>(buf + s * (kDim * 2) + ((cc ^ (s & 15)) << 4)) = kr[r];
       }
     };
-    // one 64-key tile: per column block of 32 keys, 2 row blocks x 8 K-steps of MFMA, then the
-    // epilogue (the first block's epilogue can run under the second block's MFMAs)
-    auto compute = [&](const unsigned char* cur, int kt0) {
+    // One phase = the MFMAs of one 32-key column block (2 row blocks x 8 K-steps) into (n0, n1),
+    // interleaved with the epilogue of the previous column block's accumulators (e0, e1), so
+    // the VALU work of the epilogue issues between independent MFMAs.  The epilogue sums
+    // w * ReLU over this lane's 32 heads (two ascending runs of 16, heads 32*rb + 16*hf + i)
+    // and adds the other lane half's sum.  ReLU is an integer max on the float bits: negative
+    // values and -0 are negative as int32 and become +0; non-negative values pass unchanged.
+    auto phase = [&](const unsigned char* cur, int cb, f32x16& n0, f32x16& n1, const f32x16& e0,
+                     const f32x16& e1) -> float {
+      n0 = f32x16{};
+      n1 = f32x16{};
+      float p0 = 0.f, p1 = 0.f;
+      const int s = 32 * cb + n;
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        f32x16 acc0 = f32x16{}, acc1 = f32x16{};
-        const int s = 32 * cb + n;
+      for (int j = 0; j < 8; ++j) {
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(cur + s * (kDim * 2) + (((2 * j + hf) ^ (n & 15)) << 4));
+        n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][j], kf, n0, 0, 0, 0);
+        n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][j], kf, n1, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const bf16x8 kf =
-              *reinterpret_cast<const bf16x8*>(cur + s * (kDim * 2) + (((2 * j + hf) ^ (n & 15)) << 4));
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][j], kf, acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][j], kf, acc1, 0, 0, 0);
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = 2 * j + ii;
+          p0 = __builtin_fmaf(wr[i], relu_bits(e0[i]), p0);
+          p1 = __builtin_fmaf(wr[16 + i], relu_bits(e1[i]), p1);
         }
-        // w * ReLU over this lane's 32 heads (two ascending runs of 16), then the other lane
-        // half's 32 heads.  ReLU is an integer max on the float bits: negative values and -0
-        // are negative as int32 and become +0; non-negative values pass unchanged.
-        float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p0 = __builtin_fmaf(wr[i], relu_bits(acc0[i]), p0);
-          p1 = __builtin_fmaf(wr[16 + i], relu_bits(acc1[i]), p1);
-        }
-        const float score = half_swap_sum(p0 + p1);
-        const int key = kt0 + 32 * cb + n;
-        if (hf == 0 && key < n_o) orow[key] = score;
       }
+      return half_swap_sum(p0 + p1);
+    };
+    // scores of a tile are stored after the barrier that follows it, so the store latency is
+    // covered by the next tile's work instead of by the wait before the next LDS tile write
+    // scores of (previous tile, column block 1) and (this tile, column block 0); a negative
+    // previous tile start means there is none and its store is dropped
+    auto store = [&](float s_prev, int kt_prev, float s_cur, int kt_cur) {
+      const int kp = kt_prev + 32 + n, kc = kt_cur + n;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s_prev), ors,
+                                            (hf == 0 && kt_prev >= 0) ? kp * 4 : kDropOffset, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s_cur), ors, hf == 0 ? kc * 4 : kDropOffset, 0, 0);
     };
 
     const int ntl = kend > kbeg ? ceil_div(kend - kbeg, kTileKeys) : 0;
     if (ntl > 0) gload(kregA, kbeg);
     if (ntl > 1) gload(kregB, kbeg + kTileKeys);
     if (ntl > 0) swrite(kregA, kbuf0);
+    // Everything loaded before the tile loop (query block, weights, first tiles) has landed
+    // here; saying so once keeps per-use waits on the query registers out of the loop, where
+    // they would also wait for the prefetched tiles and the score stores.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    // c0*: column block 0 of the current tile; c1*: column block 1 (of the previous tile while
+    // the current tile's block 0 is multiplied)
+    f32x16 c0a, c0b, c1a = f32x16{}, c1b = f32x16{};
+    int kt_prev = -1;
     for (int tt = 0; tt < ntl; tt += 2) {
-      const int kt0 = kbeg + tt * kTileKeys;
+      int kt0 = kbeg + tt * kTileKeys;
       // tile tt is in kbuf0, tile tt+1 is in flight in kregB, kregA is free
       if (tt + 2 < ntl) gload(kregA, kt0 + 2 * kTileKeys);
-      compute(kbuf0, kt0);
+      float s_prev = phase(kbuf0, 0, c0a, c0b, c1a, c1b);
+      float s_cur = phase(kbuf0, 1, c1a, c1b, c0a, c0b);
       if (tt + 1 < ntl) swrite(kregB, kbuf1);
       __syncthreads();
+      store(s_prev, kt_prev, s_cur, kt0);
+      kt_prev = kt0;
       if (tt + 1 >= ntl) break;
       // tile tt+1 is in kbuf1, tile tt+2 is in flight in kregA, kregB is free
-      if (tt + 3 < ntl) gload(kregB, kt0 + 3 * kTileKeys);
-      compute(kbuf1, kt0 + kTileKeys);
+      kt0 += kTileKeys;
+      if (tt + 3 < ntl) gload(kregB, kt0 + 2 * kTileKeys);
+      s_prev = phase(kbuf1, 0, c0a, c0b, c1a, c1b);
+      s_cur = phase(kbuf1, 1, c1a, c1b, c0a, c0b);
       if (tt + 2 < ntl) swrite(kregA, kbuf0);
       __syncthreads();
+      store(s_prev, kt_prev, s_cur, kt0);
+      kt_prev = kt0;
+    }
+    if (ntl > 0) {  // column block 1 of the last tile
+      float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p0 = __builtin_fmaf(wr[i], relu_bits(c1a[i]), p0);
+        p1 = __builtin_fmaf(wr[16 + i], relu_bits(c1b[i]), p1);
+      }
+      const float s_last = half_swap_sum(p0 + p1);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s_last), ors,
+                                            hf == 0 ? (kt_prev + 32 + n) * 4 : kDropOffset, 0, 0);
     }
     u = (uint32_t)slot[4 + (iter & 1)];
     ++iter;
