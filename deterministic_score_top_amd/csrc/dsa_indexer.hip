@@ -84,6 +84,7 @@ struct Call {
   int64_t ld;
   uint32_t* ctrl;
   const dsa_indexer_tuning* tuning;
+  int store_keys;
 };
 
 int launch_scores(const Call& c, hipStream_t stream) {
@@ -131,6 +132,7 @@ int launch_scores(const Call& c, hipStream_t stream) {
   p.Lmax = (int32_t)L;
   p.chunk_tiles = chunk;
   p.max_tiles = max_tiles;
+  p.store_keys = c.store_keys;
   if (dsa::launch_score(p, grid, smem, stream) != hipSuccess) return DSA_ERR_LAUNCH;
   return DSA_OK;
 }
@@ -193,13 +195,13 @@ int dsa_indexer_topk_ex(const dsa_indexer_shape* shape, const void* q, const voi
   hipEvent_t* ev = profiler ? &profiler->ev[3 * profiler->used] : nullptr;
 
   if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return DSA_ERR_LAUNCH;
-  Call c{shape, q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets, scores, ld, ctrl, tuning};
+  Call c{shape, q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets, scores, ld, ctrl, tuning, 1};
   rc = launch_scores(c, stream);
   if (rc) return rc;
   if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return DSA_ERR_LAUNCH;
 
   dsa::SelectParams sp;
-  sp.scores = scores;
+  sp.keys = reinterpret_cast<const uint32_t*>(scores);
   sp.ld = ld;
   sp.cu_q = cu_seqlens_q;
   sp.cu_k = cu_seqlens_k;
@@ -242,7 +244,7 @@ int dsa_indexer_scores(const dsa_indexer_shape* shape, const void* q, const void
   if (workspace_bytes < (size_t)dsa::kCtrlBytes) return DSA_ERR_WORKSPACE;
   if (shape->total_q == 0) return DSA_OK;
   Call c{shape, q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets, out_scores, ld_out,
-         static_cast<uint32_t*>(workspace), nullptr};
+         static_cast<uint32_t*>(workspace), nullptr, 0};
   return launch_scores(c, stream);
 }
 

@@ -43,10 +43,11 @@ struct ScoreParams {
   int32_t B, T, Tkv, Lmax;
   int32_t chunk_tiles;  // keys per unit = chunk_tiles * kTileKeys
   int32_t max_tiles;    // capacity of the LDS tile table
+  int32_t store_keys;   // 1: store order-preserving 32-bit keys instead of FP32 scores
 };
 
 struct SelectParams {
-  const float* scores;  // fp32 rows, stride ld
+  const uint32_t* keys;  // order-preserving score keys, rows of stride ld
   int64_t ld;
   const int32_t* cu_q;
   const int32_t* cu_k;

@@ -53,6 +53,15 @@ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; 
 // max(x, +0) for finite x, as one integer max on the bits (-0 and negatives map to +0).
 __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
+// Order-preserving map of an FP32 score to 32 bits: unsigned order of the keys is score order
+// (negative scores have all bits flipped, non-negative ones the sign bit set).  Sums formed
+// here never produce -0 (they start from +0 and add finite terms), so no sign canonicalisation
+// is needed.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
 // x[l] + x[l ^ 32], lower half first in every lane (v_permlane32_swap, no LDS traffic).
 __device__ __forceinline__ float half_swap_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -312,11 +321,13 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
     // covered by the next tile's work instead of by the wait before the next LDS tile write
     // scores of (previous tile, column block 1) and (this tile, column block 0); a negative
     // previous tile start means there is none and its store is dropped
+    const bool keys_out = p.store_keys != 0;
+    auto outbits = [&](float v) -> uint32_t { return keys_out ? score_key(v) : __float_as_uint(v); };
     auto store = [&](float s_prev, int kt_prev, float s_cur, int kt_cur) {
       const int kp = kt_prev + 32 + n, kc = kt_cur + n;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s_prev), ors,
+      __builtin_amdgcn_raw_buffer_store_b32(outbits(s_prev), ors,
                                             (hf == 0 && kt_prev >= 0) ? kp * 4 : kDropOffset, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s_cur), ors, hf == 0 ? kc * 4 : kDropOffset, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(outbits(s_cur), ors, hf == 0 ? kc * 4 : kDropOffset, 0, 0);
     };
 
     const int ntl = kend > kbeg ? ceil_div(kend - kbeg, kTileKeys) : 0;
@@ -361,7 +372,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
         p1 = __builtin_fmaf(wr[16 + i], relu_bits(c1b[i]), p1);
       }
       const float s_last = half_swap_sum(p0 + p1);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s_last), ors,
+      __builtin_amdgcn_raw_buffer_store_b32(outbits(s_last), ors,
                                             hf == 0 ? (kt_prev + 32 + n) * 4 : kDropOffset, 0, 0);
     }
     u = (uint32_t)slot[4 + (iter & 1)];

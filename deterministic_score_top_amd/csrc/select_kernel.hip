@@ -1,47 +1,44 @@
 // Top-k select phase of the DSA indexer scan on gfx950.
 //
-// One workgroup per query row.  Scores are compared as order-preserving 32-bit keys
-//     u = bits(score) with -0 -> +0;  key = (u >> 31) ? ~u : (u | 0x80000000)
-// so that unsigned key order is score order.  The result rule of the scan (flashinfer
-// PR #8691, description: top-k key ids per query, ties go to the larger id, result independent
-// of partitioning) is the total order (key descending, position descending) on the row; the
-// k-th element of that order is found exactly:
-//   pass 1 (row read): LDS histogram of the top 12 key bits -> bin d1 holding the k-th key;
-//   pass 2 (row read): every wave copies the keys of its span that fall in bin d1 into its own
-//          LDS region and counts its keys above the bin;
-//   LDS: two 10-bit digit histograms over the copied keys give the exact threshold key T, the
-//        number of keys equal to T and how many of them are left out (the lowest positions);
-//   pass 3 (row read): ordered write.  Wave w owns the contiguous span [w*S, (w+1)*S) of the
-//          row; its output offset is the sum of the selected counts of waves 0..w-1, and inside
-//          the wave positions are ranked with ballots and mbcnt.  No atomic decides any output
-//          position, so the output (ids ascending) is deterministic.
-// If a wave's copy region overflows, digits 2 and 3 are found with further row passes instead.
-// The row is read from the workspace rows written by the score phase (L2/MALL-resident after
-// the first pass).
+// Input rows hold order-preserving 32-bit keys of the FP32 scores (written by the score phase):
+// unsigned key order is score order.  The result rule of the scan (flashinfer PR #8691,
+// description: top-k key ids per query, ties go to the larger id, result independent of
+// partitioning) is the total order (key descending, position descending) on the row, and the
+// selected keys are written with ids ascending.
+//
+// Per row (one workgroup; workgroups loop over rows):
+//   A  a sample of the row (1/4 of it) gives a threshold theta = lower edge of the sample
+//      histogram bin that holds a rank a few standard deviations past k*m/n, so that, with
+//      overwhelming probability, theta is below the k-th key while only ~1.3k keys are >= theta;
+//   B  one pass compares every key with theta and copies the survivors (key, position) into
+//      per-wave LDS regions in position order (ballots + mbcnt, no atomics);
+//   C  the exact k-th key T is found over the survivors with range-normalised LDS histograms
+//      (11, 11, 10 bits), together with how many keys equal T and how many of those are left
+//      out (the lowest positions);
+//   D  the survivors are written in position order: wave w starts at the fixed-order sum of
+//      the selected counts of waves 0..w-1, lanes are ranked with ballots and mbcnt.
+// If the sample's guess fails (fewer than k survivors, or a region overflows), an exact
+// fallback resolves T with histograms over every key and writes from the whole row.  Results
+// never depend on which path ran.
+//
+// Passes read the row from the workspace rows written by the score phase; after the first read
+// they are L2/MALL-resident.  A row costs about 1.25 reads when the sample's guess holds.
 
 #include "dsa_internal.h"
 
 namespace dsa {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSelThreads = 512;
-constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kBits1 = 12;                 // first digit: key bits 31..20
-constexpr int kBins1 = 1 << kBits1;
-constexpr int kBits2 = 10;                 // second digit: key bits 19..10
-constexpr int kBits3 = 10;                 // third digit: key bits 9..0
-constexpr int kRegion = 512;               // copied keys per wave
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
+constexpr int kHistBits = 11;
+constexpr int kHistBins = 1 << kHistBits;
+constexpr int kCandCap = 3072;    // survivors per row held in LDS
+constexpr int kSegCache = 256;    // segments whose tables are cached in LDS
+constexpr int kSampleStride = 4;  // sample = every key of every 4th step
 
 __device__ __forceinline__ float key_value(uint32_t key) {
-  const uint32_t u = (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;
+  const uint32_t u = key ^ (~(uint32_t)((int32_t)key >> 31) | 0x80000000u);
   return __uint_as_float(u);
 }
 
@@ -62,52 +59,61 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
   for (int o = 32; o > 0; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o, 64);
   return v;
 }
-
-__device__ __forceinline__ int find_segment(const int32_t* cu_q, int B, int t) {
-  int lo = 0, hi = B + 1;  // first index with cu_q[idx] > t
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (cu_q[mid] <= t) lo = mid + 1; else hi = mid;
-  }
-  return lo - 1;
-}
-
-// Four keys at row positions pos..pos+3 (0 = no element past n).  pos is a multiple of 4 and
-// below n; the row stride is a multiple of 64 floats, so the 16-byte load stays inside the row.
-__device__ __forceinline__ void load4(const float* row, int pos, int n, uint32_t (&k)[4]) {
-  const f32x4 v = *reinterpret_cast<const f32x4*>(row + pos);
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) k[c] = (pos + c < n) ? order_key(v[c]) : 0u;
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
 }
 
-struct Smem {
-  uint32_t hist[kBins1];
-  uint32_t region[kSelWaves][kRegion];
-  uint32_t wsum[kSelWaves][4];
+template <int NT>
+struct alignas(16) Smem {
+  static constexpr int NW = NT / 64;
+  static constexpr int R = kCandCap / NW;  // survivors per wave region
+  uint32_t hist[kHistBins];
+  uint32_t ckey[NW][R];
+  uint16_t cpos[NW][R];
+  uint32_t wred[NW][4];
   uint32_t bcast[8];
+  int32_t cq[kSegCache + 1];
+  int32_t ck[kSegCache + 1];
+  int32_t off[kSegCache];
 };
 
-// Locate the bin holding rank `krem` (1-based, counted from the top) in hist[0..nb).
-// Writes bcast[0] = bin, bcast[1] = count above the bin, bcast[2] = count in the bin.
-__device__ void find_bin(Smem& sm, int nb, uint32_t krem) {
+// Locate the bin holding rank krem (1-based, from the top) in hist[0..nb): returns
+// (bin, count above it, count in it) through bcast.  Thread tid owns bins
+// [nb - (tid+1)*per, nb - tid*per).
+template <int NT>
+__device__ void find_bin(Smem<NT>& sm, int nb, uint32_t krem) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int per = (nb + kSelThreads - 1) / kSelThreads;
-  const int hi = nb - tid * per;          // this thread owns bins [lo, hi), from the top down
-  const int lo = max(hi - per, 0);
+  const int per = nb >= NT ? nb / NT : 1;
+  const int lo = nb - (tid + 1) * per;
   uint32_t local = 0;
-  for (int d = hi - 1; d >= lo; --d) local += sm.hist[d];
+  if (lo >= 0) {
+    if (per == 4) {
+      const u32x4 h = *reinterpret_cast<const u32x4*>(&sm.hist[lo]);
+      local = h[0] + h[1] + h[2] + h[3];
+    } else {
+      for (int d = 0; d < per; ++d) local += sm.hist[lo + d];
+    }
+  }
   uint32_t incl = local;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const uint32_t y = __shfl_up(incl, o, 64);
     if (lane >= o) incl += y;
   }
-  if (lane == 63) sm.wsum[wv][0] = incl;
+  if (lane == 63) sm.wred[wv][0] = incl;
   __syncthreads();
   uint32_t above = incl - local;
-  for (int i = 0; i < wv; ++i) above += sm.wsum[i][0];
-  if (hi > 0 && above < krem && krem <= above + local) {
-    for (int d = hi - 1; d >= lo; --d) {
+#pragma unroll
+  for (int i = 0; i < Smem<NT>::NW; ++i) above += i < wv ? sm.wred[i][0] : 0u;
+  if (lo >= 0 && above < krem && krem <= above + local) {
+    for (int d = lo + per - 1; d >= lo; --d) {
       const uint32_t h = sm.hist[d];
       if (krem <= above + h) {
         sm.bcast[0] = (uint32_t)d;
@@ -121,216 +127,403 @@ __device__ void find_bin(Smem& sm, int nb, uint32_t krem) {
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
-  __shared__ Smem sm;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int t = blockIdx.x;
-  const int topk = p.topk;
-  int32_t* const oid = p.out_ids + (int64_t)t * topk;
-  float* const osc = p.out_scores + (int64_t)t * topk;
+// Row keys seen by one lane: positions base + 256*s + 4*lane + c of the wave's span, read from
+// the row on every pass (the rows stay L2/MALL-resident between passes).
+struct Keys {
+  const uint32_t* row;
+  int n, base, span;
 
-  int n = 0, kb = 0;
-  if (!(p.ctrl[kCtrlStatus] & kStatusBadSegments)) {
-    const int b = find_segment(p.cu_q, p.B, t);
-    if (b >= 0 && b < p.B) {
-      const int cq = p.cu_q[b];
-      const int lk = min(p.cu_k[b + 1] - p.cu_k[b], p.Lmax);
-      const int off = p.offs ? p.offs[b] : 0;
-      kb = p.cu_k[b];
-      n = min(max(off + (t - cq) + 1, 0), max(lk, 0));
-    }
-  }
-  const float* const row = p.scores + (int64_t)t * p.ld;
-
-  if (n <= topk) {  // every visible key is kept; pad the rest
-    for (int j = tid; j < topk; j += kSelThreads) {
-      if (j < n) {
-        oid[j] = kb + j;
-        osc[j] = key_value(order_key(row[j]));
-      } else {
-        oid[j] = -1;
-        osc[j] = -__builtin_inff();
-      }
-    }
-    return;
-  }
-
-  // wave spans: [wv*span, wv*span + span), span a multiple of 256, lane owns 4 consecutive
-  const int span = ((n + kSelWaves * 256 - 1) / (kSelWaves * 256)) * 256;
-  const int base = wv * span;
-  const int wend = min(base + span, n);
-
-  // ---- pass 1: histogram of the top 12 key bits ---------------------------------------------
-  for (int i = tid; i < kBins1; i += kSelThreads) sm.hist[i] = 0u;
-  __syncthreads();
-  for (int pos0 = base; pos0 < wend; pos0 += 256) {
-    const int pos = pos0 + 4 * lane;
-    uint32_t k4[4] = {0u, 0u, 0u, 0u};
-    if (pos < n) load4(row, pos, n, k4);
+  __device__ void load4(int pos, uint32_t (&o)[4]) const {
+    if (pos < n) {
+      // pos is a multiple of 4 below n and the row stride a multiple of 64 keys: in the row
+      const u32x4 v = *reinterpret_cast<const u32x4*>(row + pos);
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (k4[c]) atomicAdd(&sm.hist[k4[c] >> (32 - kBits1)], 1u);
+      for (int c = 0; c < 4; ++c) o[c] = (pos + c < n) ? v[c] : 0u;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = 0u;
+    }
   }
-  __syncthreads();
-  find_bin(sm, kBins1, (uint32_t)topk);
-  const uint32_t d1 = sm.bcast[0];
-  uint32_t krem = (uint32_t)topk - sm.bcast[1];
-  const uint32_t in_bin1 = sm.bcast[2];
+  // f(position of c=0, keys[4]) for every `stride`-th step of the span, in order (wave-uniform)
+  template <class F>
+  __device__ void each(F&& f, int stride = 1) const {
+    const int lane = threadIdx.x & 63;
+    for (int s = 0; 256 * s < span; s += stride) {
+      uint32_t t[4];
+      load4(base + 256 * s + 4 * lane, t);
+      f(base + 256 * s + 4 * lane, t);
+    }
+  }
+};
 
-  // ---- pass 2: copy the keys of bin d1 into this wave's region; count keys above the bin ----
-  uint32_t above_w = 0, ncopy = 0;
-  for (int pos0 = base; pos0 < wend; pos0 += 256) {
-    const int pos = pos0 + 4 * lane;
-    uint32_t k4[4] = {0u, 0u, 0u, 0u};
-    if (pos < n) load4(row, pos, n, k4);
-    uint32_t cnt = 0;
+// Exact fallback: T from histograms over all keys of the row; returns T and eq_skip, and the
+// per-wave counts of keys > T and == T in wred[wv][2], wred[wv][3].
+template <int NT, class KS>
+__device__ void resolve_all(Smem<NT>& sm, const KS& ks, int topk, uint32_t& T, uint32_t& eq_skip) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint32_t mn = 0xffffffffu, mx = 0u, cnt = 0;
+  ks.each([&](int, const uint32_t (&k4)[4]) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint32_t dg = k4[c] >> (32 - kBits1);
-      above_w += (k4[c] && dg > d1) ? 1u : 0u;
-      cnt += (k4[c] && dg == d1) ? 1u : 0u;
+      mn = min(mn, k4[c] - 1u);  // invalid (0) wraps to the top and drops out
+      mx = max(mx, k4[c]);
+      cnt += k4[c] ? 1u : 0u;
     }
-    uint32_t ex, tot;
-    wave_prefix3(cnt, ex, tot);
-    uint32_t slot = ncopy + ex;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (k4[c] && (k4[c] >> (32 - kBits1)) == d1) {
-        if (slot < (uint32_t)kRegion) sm.region[wv][slot] = k4[c];
-        ++slot;
-      }
-    }
-    ncopy += tot;
+  });
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  cnt = wave_sum(cnt);
+  if (lane == 0) {
+    sm.wred[wv][1] = mn;
+    sm.wred[wv][2] = mx;
+    sm.wred[wv][3] = cnt;
   }
-  above_w = wave_sum(above_w);
-  if (lane == 0) sm.wsum[wv][1] = ncopy;
   __syncthreads();
-  bool overflow = false;
-  for (int i = 0; i < kSelWaves; ++i) overflow |= sm.wsum[i][1] > (uint32_t)kRegion;
-  __syncthreads();
-
-  // ---- digits 2 and 3: from the copied keys, or by further row passes on overflow ------------
-  uint32_t prefix = d1;
-  uint32_t eq_total = in_bin1;
-  int shift = 32 - kBits1;
+  uint32_t valid = 0;
 #pragma unroll
-  for (int dg = 0; dg < 2; ++dg) {
-    const int bits = dg == 0 ? kBits2 : kBits3;
+  for (int i = 0; i < Smem<NT>::NW; ++i) {
+    mn = min(mn, sm.wred[i][1]);
+    mx = max(mx, sm.wred[i][2]);
+    valid += sm.wred[i][3];
+  }
+  const uint32_t kmin = mn + 1u;
+  const uint32_t range = mx - kmin;
+  int shift = range ? 32 - __clz((int)range) : 0;
+  uint32_t prefix = 0, krem = (uint32_t)topk, eq_total = valid;  // all equal if no digit left
+  bool first = true;
+  __syncthreads();
+  while (shift > 0) {
+    const int bits = min(kHistBits, shift);
     shift -= bits;
     const uint32_t nb = 1u << bits;
-    for (int i = tid; i < (int)nb; i += kSelThreads) sm.hist[i] = 0u;
+    for (int i = tid; i < (int)nb; i += NT) sm.hist[i] = 0u;
     __syncthreads();
-    if (!overflow) {
-      const uint32_t m = min(sm.wsum[wv][1], (uint32_t)kRegion);
-      for (uint32_t i = lane; i < m; i += 64) {
-        const uint32_t kk = sm.region[wv][i];
-        if ((kk >> (shift + bits)) == prefix) atomicAdd(&sm.hist[(kk >> shift) & (nb - 1u)], 1u);
-      }
-    } else {
-      for (int pos = base + 4 * lane; pos < wend; pos += 256) {
-        uint32_t k4[4];
-        load4(row, pos, n, k4);
+    ks.each([&](int, const uint32_t (&k4)[4]) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (k4[c] && (k4[c] >> (shift + bits)) == prefix)
-            atomicAdd(&sm.hist[(k4[c] >> shift) & (nb - 1u)], 1u);
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t v = k4[c] - kmin;
+        if (k4[c] && (first || (uint32_t)((uint64_t)v >> (shift + bits)) == prefix))
+          atomicAdd(&sm.hist[(v >> shift) & (nb - 1u)], 1u);
       }
-    }
+    });
     __syncthreads();
-    find_bin(sm, (int)nb, krem);
+    find_bin<NT>(sm, (int)nb, krem);
     prefix = (prefix << bits) | sm.bcast[0];
     krem -= sm.bcast[1];
     eq_total = sm.bcast[2];
+    first = false;
     __syncthreads();
   }
-  const uint32_t thr = prefix;                 // key of the k-th element
-  const uint32_t eq_skip = eq_total - krem;    // keys equal to thr left out (lowest positions)
-
-  // ---- per-wave counts of keys above thr and equal to thr ------------------------------------
-  uint32_t gt_w = 0, eq_w = 0;
-  if (!overflow) {
-    const uint32_t m = sm.wsum[wv][1];
-    for (uint32_t i = lane; i < m; i += 64) {
-      const uint32_t kk = sm.region[wv][i];
-      gt_w += kk > thr ? 1u : 0u;
-      eq_w += kk == thr ? 1u : 0u;
-    }
-    gt_w = wave_sum(gt_w) + above_w;
-  } else {
-    for (int pos = base + 4 * lane; pos < wend; pos += 256) {
-      uint32_t k4[4];
-      load4(row, pos, n, k4);
+  T = kmin + prefix;
+  eq_skip = eq_total - krem;
+  uint32_t gt = 0, eq = 0;
+  ks.each([&](int, const uint32_t (&k4)[4]) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        gt_w += (k4[c] && k4[c] > thr) ? 1u : 0u;
-        eq_w += (k4[c] && k4[c] == thr) ? 1u : 0u;
-      }
+    for (int c = 0; c < 4; ++c) {
+      gt += (k4[c] && k4[c] > T) ? 1u : 0u;
+      eq += (k4[c] && k4[c] == T) ? 1u : 0u;
     }
-    gt_w = wave_sum(gt_w);
-  }
-  eq_w = wave_sum(eq_w);
+  });
+  gt = wave_sum(gt);
+  eq = wave_sum(eq);
   if (lane == 0) {
-    sm.wsum[wv][2] = gt_w;
-    sm.wsum[wv][3] = eq_w;
+    sm.wred[wv][2] = gt;
+    sm.wred[wv][3] = eq;
   }
   __syncthreads();
-  uint32_t eq_base = 0, sel_base = 0;
-  for (int i = 0; i < wv; ++i) {
-    const uint32_t g_i = sm.wsum[i][2], e_i = sm.wsum[i][3];
-    const uint32_t take = (eq_base + e_i > eq_skip) ? min(e_i, eq_base + e_i - eq_skip) : 0u;
-    sel_base += g_i + take;
-    eq_base += e_i;
-  }
+}
 
-  // ---- pass 3: ordered write ----------------------------------------------------------------
-  uint32_t eq_run = eq_base, sel_run = sel_base;
-  for (int pos0 = base; pos0 < wend; pos0 += 256) {
-    const int pos = pos0 + 4 * lane;
-    uint32_t k4[4] = {0u, 0u, 0u, 0u};
-    if (pos < n) load4(row, pos, n, k4);
-    bool eqf[4], gtf[4];
-    uint32_t eqc = 0;
+// Output offsets of this wave: selected keys of waves before it, and equal keys before it.
+template <int NT>
+__device__ void wave_bases(Smem<NT>& sm, uint32_t eq_skip, uint32_t& sel_base, uint32_t& eq_base) {
+  const int wv = threadIdx.x >> 6;
+  sel_base = 0;
+  eq_base = 0;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      eqf[c] = k4[c] && k4[c] == thr;
-      gtf[c] = k4[c] && k4[c] > thr;
-      eqc += eqf[c] ? 1u : 0u;
+  for (int i = 0; i < Smem<NT>::NW; ++i) {
+    if (i < wv) {
+      const uint32_t g_i = sm.wred[i][2], e_i = sm.wred[i][3];
+      const uint32_t take = (eq_base + e_i > eq_skip) ? min(e_i, eq_base + e_i - eq_skip) : 0u;
+      sel_base += g_i + take;
+      eq_base += e_i;
     }
-    uint32_t eq_ex, eq_tot;
-    wave_prefix3(eqc, eq_ex, eq_tot);
-    bool self[4];
-    uint32_t selc = 0;
-    uint32_t er = eq_run + eq_ex;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      self[c] = gtf[c] || (eqf[c] && er >= eq_skip);
-      er += eqf[c] ? 1u : 0u;
-      selc += self[c] ? 1u : 0u;
+  }
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
+  constexpr int NW = NT / 64;
+  constexpr int R = Smem<NT>::R;
+  __shared__ Smem<NT> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int topk = p.topk;
+  const bool bad = (p.ctrl[kCtrlStatus] & kStatusBadSegments) != 0;
+  const bool cached = p.B <= kSegCache;
+  if (cached) {
+    for (int i = tid; i <= p.B; i += NT) {
+      sm.cq[i] = p.cu_q[i];
+      sm.ck[i] = p.cu_k[i];
+      if (i < p.B) sm.off[i] = p.offs ? p.offs[i] : 0;
     }
-    uint32_t sel_ex, sel_tot;
-    wave_prefix3(selc, sel_ex, sel_tot);
-    uint32_t slot = sel_run + sel_ex;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (self[c] && slot < (uint32_t)topk) {  // exactly topk are selected; the bound is a guard
-        oid[slot] = kb + pos + c;
-        osc[slot] = key_value(k4[c]);
-        ++slot;
+  }
+  __syncthreads();
+
+  for (int t = blockIdx.x; t < p.T; t += gridDim.x) {
+    // ---- row geometry ----------------------------------------------------------------------
+    int n = 0, kb = 0;
+    if (!bad) {
+      const int32_t* cq = cached ? sm.cq : p.cu_q;
+      int lo = 0, hi = p.B + 1;  // first segment start beyond t
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (cq[mid] <= t) lo = mid + 1; else hi = mid;
+      }
+      const int b = lo - 1;
+      if (b >= 0 && b < p.B) {
+        const int qb = cq[b];
+        kb = cached ? sm.ck[b] : p.cu_k[b];
+        const int lk = min((cached ? sm.ck[b + 1] : p.cu_k[b + 1]) - kb, p.Lmax);
+        const int off = cached ? sm.off[b] : (p.offs ? p.offs[b] : 0);
+        n = min(max(off + (t - qb) + 1, 0), max(lk, 0));
       }
     }
-    eq_run += eq_tot;
-    sel_run += sel_tot;
+    const uint32_t* const row = p.keys + (int64_t)t * p.ld;
+    int32_t* const oid = p.out_ids + (int64_t)t * topk;
+    float* const osc = p.out_scores + (int64_t)t * topk;
+    if (n <= topk) {  // every visible key is kept; pad the rest
+      for (int j = tid; j < topk; j += NT) {
+        if (j < n) {
+          oid[j] = kb + j;
+          osc[j] = key_value(row[j]);
+        } else {
+          oid[j] = -1;
+          osc[j] = -__builtin_inff();
+        }
+      }
+      continue;
+    }
+
+    Keys ks;
+    ks.row = row;
+    ks.n = n;
+    ks.span = ((n + NW * 256 - 1) / (NW * 256)) * 256;
+    ks.base = wv * ks.span;
+
+    // ---- A: threshold from a sample: every key of every 4th step of each wave's span --------
+    uint32_t smin = 0xffffffffu, smax = 0u, scnt = 0;
+    ks.each([&](int, const uint32_t (&k4)[4]) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        smin = min(smin, k4[c] - 1u);  // invalid (0) wraps to the top and drops out
+        smax = max(smax, k4[c]);
+        scnt += k4[c] ? 1u : 0u;
+      }
+    }, kSampleStride);
+    smin = wave_min(smin);
+    smax = wave_max(smax);
+    scnt = wave_sum(scnt);
+    if (lane == 0) {
+      sm.wred[wv][1] = smin;
+      sm.wred[wv][2] = smax;
+      sm.wred[wv][3] = scnt;
+    }
+    __syncthreads();
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      smin = min(smin, sm.wred[i][1]);
+      smax = max(smax, sm.wred[i][2]);
+      m += sm.wred[i][3];
+    }
+    smin += 1u;
+    // sample rank whose bin edge becomes theta: k*m/n plus 4 standard deviations and a margin
+    const float expect = (float)topk * (float)m / (float)n;
+    const uint32_t r = (uint32_t)(expect + 4.f * __builtin_sqrtf(expect) + 8.f);
+    uint32_t theta = 1u;  // every real key is >= 0x007fffff
+    __syncthreads();
+    if (m >= 64 && r < m && smax > smin) {
+      const uint32_t srange = smax - smin;
+      const int sbits = 32 - __clz((int)srange);
+      const int sshift = max(sbits - kHistBits, 0);
+      for (int i = tid; i < kHistBins; i += NT) sm.hist[i] = 0u;
+      __syncthreads();
+      ks.each([&](int, const uint32_t (&k4)[4]) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (k4[c]) atomicAdd(&sm.hist[(k4[c] - smin) >> sshift], 1u);
+      }, kSampleStride);
+      __syncthreads();
+      find_bin<NT>(sm, kHistBins, r);
+      theta = smin + (sm.bcast[0] << sshift);
+      __syncthreads();
+    }
+
+    // ---- B: keys >= theta into this wave's region, in position order ---------------------------
+    uint32_t run = 0;
+    ks.each([&](int pos, const uint32_t (&k4)[4]) {
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) cnt += k4[c] >= theta ? 1u : 0u;
+      uint32_t ex, tot;
+      wave_prefix3(cnt, ex, tot);
+      if (tot) {
+        uint32_t slot = run + ex;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (k4[c] >= theta) {
+            if (slot < (uint32_t)R) {
+              sm.ckey[wv][slot] = k4[c];
+              sm.cpos[wv][slot] = (uint16_t)(pos + c);
+            }
+            ++slot;
+          }
+        }
+      }
+      run += tot;
+    });
+    if (lane == 0) sm.wred[wv][1] = run;
+    __syncthreads();
+    uint32_t total = 0;
+    bool overflow = false;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      total += sm.wred[i][1];
+      overflow |= sm.wred[i][1] > (uint32_t)R;
+    }
+    const uint32_t mine = min(run, (uint32_t)R);
+    __syncthreads();
+
+    uint32_t T, eq_skip, sel_base, eq_base;
+    if (!overflow && total >= (uint32_t)topk) {
+      // ---- C: exact k-th key among the survivors ---------------------------------------------
+      uint32_t cmax = 0;
+      for (uint32_t i = lane; i < mine; i += 64) cmax = max(cmax, sm.ckey[wv][i]);
+      cmax = wave_max(cmax);
+      if (lane == 0) sm.wred[wv][2] = cmax;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < NW; ++i) cmax = max(cmax, sm.wred[i][2]);
+      const uint32_t range = cmax - theta;
+      int shift = range ? 32 - __clz((int)range) : 0;
+      uint32_t prefix = 0, krem = (uint32_t)topk, eq_total = total;
+      bool first = true;
+      __syncthreads();
+      while (shift > 0) {
+        const int bits = min(kHistBits, shift);
+        shift -= bits;
+        const uint32_t nb = 1u << bits;
+        for (int i = tid; i < (int)nb; i += NT) sm.hist[i] = 0u;
+        __syncthreads();
+        for (uint32_t i = lane; i < mine; i += 64) {
+          const uint32_t v = sm.ckey[wv][i] - theta;
+          if (first || (uint32_t)((uint64_t)v >> (shift + bits)) == prefix)
+            atomicAdd(&sm.hist[(v >> shift) & (nb - 1u)], 1u);
+        }
+        __syncthreads();
+        find_bin<NT>(sm, (int)nb, krem);
+        prefix = (prefix << bits) | sm.bcast[0];
+        krem -= sm.bcast[1];
+        eq_total = sm.bcast[2];
+        first = false;
+        __syncthreads();
+      }
+      T = theta + prefix;
+      eq_skip = eq_total - krem;
+      uint32_t gt = 0, eq = 0;
+      for (uint32_t i = lane; i < mine; i += 64) {
+        const uint32_t kk = sm.ckey[wv][i];
+        gt += kk > T ? 1u : 0u;
+        eq += kk == T ? 1u : 0u;
+      }
+      gt = wave_sum(gt);
+      eq = wave_sum(eq);
+      if (lane == 0) {
+        sm.wred[wv][2] = gt;
+        sm.wred[wv][3] = eq;
+      }
+      __syncthreads();
+      wave_bases<NT>(sm, eq_skip, sel_base, eq_base);
+      // ---- D: ordered write from the survivors ------------------------------------------------
+      uint32_t eq_run = eq_base, sel_run = sel_base;
+      for (uint32_t i0 = 0; i0 < mine; i0 += 64) {
+        const uint32_t i = i0 + lane;
+        const bool live = i < mine;
+        const uint32_t kk = live ? sm.ckey[wv][i] : 0u;
+        const bool eqf = live && kk == T;
+        const bool gtf = live && kk > T;
+        const uint64_t eqm = __ballot(eqf);
+        const bool self = gtf || (eqf && eq_run + lanes_below(eqm) >= eq_skip);
+        const uint64_t selm = __ballot(self);
+        const uint32_t slot = sel_run + lanes_below(selm);
+        if (self && slot < (uint32_t)topk) {  // exactly topk are selected; the bound is a guard
+          oid[slot] = kb + (int)sm.cpos[wv][i];
+          osc[slot] = key_value(kk);
+        }
+        eq_run += (uint32_t)__popcll(eqm);
+        sel_run += (uint32_t)__popcll(selm);
+      }
+    } else {
+      // ---- exact fallback over every key ------------------------------------------------------
+      resolve_all<NT>(sm, ks, topk, T, eq_skip);
+      wave_bases<NT>(sm, eq_skip, sel_base, eq_base);
+      uint32_t eq_run = eq_base, sel_run = sel_base;
+      ks.each([&](int pos, const uint32_t (&k4)[4]) {
+        bool eqf[4], gtf[4];
+        uint32_t eqc = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          eqf[c] = k4[c] && k4[c] == T;
+          gtf[c] = k4[c] && k4[c] > T;
+          eqc += eqf[c] ? 1u : 0u;
+        }
+        uint32_t eq_ex, eq_tot;
+        wave_prefix3(eqc, eq_ex, eq_tot);
+        bool self[4];
+        uint32_t selc = 0;
+        uint32_t er = eq_run + eq_ex;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          self[c] = gtf[c] || (eqf[c] && er >= eq_skip);
+          er += eqf[c] ? 1u : 0u;
+          selc += self[c] ? 1u : 0u;
+        }
+        uint32_t sel_ex, sel_tot;
+        wave_prefix3(selc, sel_ex, sel_tot);
+        uint32_t slot = sel_run + sel_ex;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (self[c] && slot < (uint32_t)topk) {
+            oid[slot] = kb + pos + c;
+            osc[slot] = key_value(k4[c]);
+            ++slot;
+          }
+        }
+        eq_run += eq_tot;
+        sel_run += sel_tot;
+      });
+    }
+    __syncthreads();  // LDS is reused by the next row
   }
+}
+
+template <int NT>
+hipError_t launch_variant(const SelectParams& p, hipStream_t s) {
+  int dev = 0, cus = 0, bpc = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipErrorInvalidDevice;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, select_kernel<NT>, NT, 0) != hipSuccess || bpc < 1)
+    bpc = 1;
+  const int grid = min(p.T, cus * bpc * 4);
+  hipLaunchKernelGGL((select_kernel<NT>), dim3(grid), dim3(NT), 0, s, p);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_select(const SelectParams& p, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_kernel, dim3(p.T), dim3(kSelThreads), 0, s, p);
-  return hipGetLastError();
+  return launch_variant<256>(p, s);
 }
 
 }  // namespace dsa

@@ -74,6 +74,16 @@ def test_ragged_segments(case):
     _check_all(W.random_segments(ql, kl, offs, topk, seed=case))
 
 
+def test_many_segments():
+    # more segments than the select kernel caches in LDS; empty and keyless segments mixed in
+    rng = np.random.default_rng(21)
+    B = 1100
+    ql = rng.integers(0, 3, B).tolist()
+    kl = rng.integers(0, 40, B).tolist()
+    offs = rng.integers(0, 50, B).tolist()
+    _check_all(W.random_segments(ql, kl, offs, topk=8, seed=21))
+
+
 @pytest.mark.parametrize("distinct", [None, 16, 2])
 def test_integer_inputs_exact(distinct):
     wl = W.integer_valued([37, 20], [300, 129], [100, 5], topk=40, seed=3, distinct_keys=distinct)
