@@ -94,9 +94,11 @@ __device__ void find_bin(Smem<NT>& sm, int nb, uint32_t krem) {
   const int lo = nb - (tid + 1) * per;
   uint32_t local = 0;
   if (lo >= 0) {
-    if (per == 4) {
-      const u32x4 h = *reinterpret_cast<const u32x4*>(&sm.hist[lo]);
-      local = h[0] + h[1] + h[2] + h[3];
+    if (per >= 4) {  // contiguous 16-byte reads: lanes cover consecutive bytes, no bank conflicts
+      for (int d = 0; d < per; d += 4) {
+        const u32x4 h = *reinterpret_cast<const u32x4*>(&sm.hist[lo + d]);
+        local += h[0] + h[1] + h[2] + h[3];
+      }
     } else {
       for (int d = 0; d < per; ++d) local += sm.hist[lo + d];
     }
@@ -426,6 +428,38 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
         eq_total = sm.bcast[2];
         first = false;
         __syncthreads();
+        if (shift > 0 && eq_total <= 64u) {
+          // Few keys left in the bin: rank them directly.  Gather them (any order) and let lane
+          // i of wave 0 count how many are greater / greater-or-equal than key i.
+          if (tid == 0) sm.bcast[3] = 0u;
+          __syncthreads();
+          for (uint32_t i = lane; i < mine; i += 64) {
+            const uint32_t kk = sm.ckey[wv][i];
+            if (((kk - theta) >> shift) == prefix) sm.hist[atomicAdd(&sm.bcast[3], 1u)] = kk;
+          }
+          __syncthreads();
+          if (wv == 0) {
+            const uint32_t c = eq_total;
+            const uint32_t mykey = (uint32_t)lane < c ? sm.hist[lane] : 0u;
+            uint32_t gt = 0, ge = 0;
+            for (uint32_t j = 0; j < c; ++j) {
+              const uint32_t o = sm.hist[j];
+              gt += o > mykey ? 1u : 0u;
+              ge += o >= mykey ? 1u : 0u;
+            }
+            if ((uint32_t)lane < c && gt < krem && krem <= ge) {  // every such lane holds the same key
+              sm.bcast[4] = mykey;
+              sm.bcast[5] = gt;
+              sm.bcast[6] = ge - gt;
+            }
+          }
+          __syncthreads();
+          prefix = sm.bcast[4] - theta;
+          krem -= sm.bcast[5];
+          eq_total = sm.bcast[6];
+          shift = 0;
+          __syncthreads();
+        }
       }
       T = theta + prefix;
       eq_skip = eq_total - krem;
