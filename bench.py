@@ -11,6 +11,9 @@ around each kernel during the timed steps), and the FP64 oracle timed on a
 bounded row sample on the host cores.
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -21,6 +24,66 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense BF16 MFMA
 FLOP_PER_PAIR = 2 * 64 * 128   # one 64x128 by 128x1 contraction per visible (query, key) pair
+SCORE_SRC = os.path.join(ROOT, "deterministic_score_top_amd", "csrc", "score_kernel.hip")
+COPY_BYTES = 512 << 20         # plain copy used to calibrate the FETCH_SIZE / WRITE_SIZE counters
+
+
+def score_kernel_hash():
+    return hashlib.sha256(open(SCORE_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_file(config):
+    return os.path.join(ROOT, "profiles", f"score_kernel_traffic_{config}.json")
+
+
+def load_traffic(config):
+    """HBM bytes per score-kernel launch from committed counter runs, if the kernel is unchanged."""
+    try:
+        rec = json.load(open(traffic_file(config)))
+    except (OSError, ValueError):
+        return None
+    if rec.get("score_kernel_sha256_16") != score_kernel_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def _pmc_avg(run_dir, counter, kernel_substr):
+    vals = []
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"].lower():
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} samples for {kernel_substr} under {run_dir}")
+    return sum(vals) / len(vals)
+
+
+def ingest_traffic(config, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """Write profiles/score_kernel_traffic_<config>.json from four rocprofv3 --pmc runs."""
+    copy_kernel = "copy"
+    f_copy = _pmc_avg(copy_fetch_dir, "FETCH_SIZE", copy_kernel)   # KiB per dispatch
+    w_copy = _pmc_avg(copy_write_dir, "WRITE_SIZE", copy_kernel)
+    f_scale = COPY_BYTES / (f_copy * 1024.0)     # true bytes per counted byte
+    w_scale = COPY_BYTES / (w_copy * 1024.0)
+    f = _pmc_avg(fetch_dir, "FETCH_SIZE", "score_kernel") * 1024.0 * f_scale
+    w = _pmc_avg(write_dir, "WRITE_SIZE", "score_kernel") * 1024.0 * w_scale
+    rec = {"config": config, "score_kernel_sha256_16": score_kernel_hash(),
+           "fetch_bytes_per_launch": f, "write_bytes_per_launch": w, "bytes_per_launch": f + w,
+           "copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": f_copy, "write_kib": w_copy,
+                                "fetch_scale": f_scale, "write_scale": w_scale}}
+    json.dump(rec, open(traffic_file(config), "w"), indent=1)
+    print(json.dumps(rec))
+
+
+def copy_calibration(reps=5):
+    """A plain device-to-device copy of COPY_BYTES, for counter calibration under rocprofv3."""
+    import torch
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {COPY_BYTES} bytes x {reps}", flush=True)
 
 
 def visible_pairs(wl):
@@ -36,7 +99,7 @@ def visible_pairs(wl):
 
 
 def cpu_baseline(wl, ids, sc, budget_s):
-    """FP64 oracle on evenly spaced rows; also checks those rows of the GPU output."""
+    """FP64 oracle on the workload's rows until the time budget is spent; also checks those rows of the GPU output."""
     import numpy as np
     from oracle import dsa_oracle as O
     from tests.parity import check_rows
@@ -48,8 +111,7 @@ def cpu_baseline(wl, ids, sc, budget_s):
     q64, k64, w64 = O.from_torch(wl.q, wl.k, wl.w)
     cu_q, cu_k = wl.cu_seqlens_q.numpy(), wl.cu_seqlens_k.numpy()
     offs = None if wl.q_pos_offsets is None else wl.q_pos_offsets.numpy()
-    stride = max(1, wl.T // 1024)
-    order = list(range(stride // 2, wl.T, stride))
+    order = np.random.default_rng(0).permutation(wl.T).tolist()   # every row, in a seeded random order
     done = []
     t0 = time.perf_counter()
     res = ([], [], [])
@@ -66,23 +128,34 @@ def cpu_baseline(wl, ids, sc, budget_s):
     except AssertionError as e:
         ok = False
         print(f"bench: sampled parity FAILED: {e}", file=sys.stderr)
+    what = "all" if len(done) == wl.T else "a seeded random sample of"
     return {"value": len(done) / el, "unit": "queries/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"{len(done)} rows (every {stride}th row from {stride // 2}) of the same workload, "
+            "sample": f"{what} {len(done)} of {wl.T} query rows of the same workload, one oracle call per row, "
                       f"{el:.1f} s, FP64 NumPy, host cpu_count={os.cpu_count()}"}, ok
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="causal_n8192")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain copy of known size (counter calibration)")
+    ap.add_argument("--ingest-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write the score-kernel traffic record from rocprofv3 --pmc output directories")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_traffic(args.config, *args.ingest_pmc)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the scan shards by queries across GPUs, see the design notes)", file=sys.stderr)
+              "(the scan shards by queries; a multi-GPU driver is not part of this library)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -148,7 +221,7 @@ def main():
         "select_kernel_ms": select_avg_ms,
         "roofline": {"bound": "mfma", "kernel": "score_kernel", "achieved": eff_score,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": eff_score / PEAK_BF16_TFLOPS,
-                     "traffic": None},
+                     "traffic": load_traffic(args.config)},
     }
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()
