@@ -36,6 +36,7 @@ constexpr int kHistBins = 1 << kHistBits;
 constexpr int kCandCap = 3072;    // survivors per row held in LDS
 constexpr int kSegCache = 256;    // segments whose tables are cached in LDS
 constexpr int kSampleStride = 4;  // sample = every key of every 4th step
+constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor word 3: raw 32-bit data, range-checked
 
 __device__ __forceinline__ float key_value(uint32_t key) {
   const uint32_t u = key ^ (~(uint32_t)((int32_t)key >> 31) | 0x80000000u);
@@ -54,19 +55,49 @@ __device__ __forceinline__ void wave_prefix3(uint32_t cnt, uint32_t& excl, uint3
   total = (uint32_t)__popcll(b0) + 2u * (uint32_t)__popcll(b1) + 4u * (uint32_t)__popcll(b2);
 }
 
+// Wave-wide reductions and scans with DPP lane moves (no LDS round trips).  update_dpp keeps
+// `old` in lanes whose row is masked off or whose source lane lies outside the row, so `old`
+// is the operation's identity.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+constexpr int kDppQuad1032 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuad2301 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowMirror = 0x140;     // lane i of a row of 16 reads lane 15-i
+constexpr int kDppRowHalfMirror = 0x141; // lane i of a half row of 8 reads lane 7-i
+constexpr int kDppRowBcast15 = 0x142;    // lane 15 of each row feeds the next row
+constexpr int kDppRowBcast31 = 0x143;    // lane 31 feeds rows 2 and 3
+constexpr int kDppRowShr = 0x110;        // + n: lane i reads lane i-n of its row
+
+// After the six steps lane 63 holds the combination of all 64 lanes.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, uint32_t identity, Op op) {
+  v = op(v, dpp<kDppQuad1032>(identity, v));
+  v = op(v, dpp<kDppQuad2301>(identity, v));
+  v = op(v, dpp<kDppRowHalfMirror>(identity, v));
+  v = op(v, dpp<kDppRowMirror>(identity, v));
+  v = op(v, dpp<kDppRowBcast15, 0xA>(identity, v));
+  v = op(v, dpp<kDppRowBcast31, 0xC>(identity, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o, 64);
-  return v;
+  return wave_reduce(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
 }
 __device__ __forceinline__ uint32_t wave_min(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  return v;
+  return wave_reduce(v, 0xffffffffu, [](uint32_t a, uint32_t b) { return min(a, b); });
 }
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return wave_reduce(v, 0u, [](uint32_t a, uint32_t b) { return max(a, b); });
+}
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += dpp<kDppRowShr + 1>(0u, v);
+  v += dpp<kDppRowShr + 2>(0u, v);
+  v += dpp<kDppRowShr + 4>(0u, v);
+  v += dpp<kDppRowShr + 8>(0u, v);
+  v += dpp<kDppRowBcast15, 0xA>(0u, v);
+  v += dpp<kDppRowBcast31, 0xC>(0u, v);
   return v;
 }
 
@@ -77,7 +108,9 @@ struct alignas(16) Smem {
   uint32_t hist[kHistBins];
   uint32_t ckey[NW][R];
   uint16_t cpos[NW][R];
-  uint32_t wred[NW][4];
+  // per-wave partials: [0] find_bin, [1..3] fallback statistics, [2..3] selected/equal counts,
+  // [4..6] sample statistics, [7..8] compaction count and row maximum
+  uint32_t wred[NW][12];
   uint32_t bcast[8];
   int32_t cq[kSegCache + 1];
   int32_t ck[kSegCache + 1];
@@ -103,12 +136,7 @@ __device__ void find_bin(Smem<NT>& sm, int nb, uint32_t krem) {
       for (int d = 0; d < per; ++d) local += sm.hist[lo + d];
     }
   }
-  uint32_t incl = local;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
+  const uint32_t incl = wave_incl_scan(local);
   if (lane == 63) sm.wred[wv][0] = incl;
   __syncthreads();
   uint32_t above = incl - local;
@@ -130,30 +158,33 @@ __device__ void find_bin(Smem<NT>& sm, int nb, uint32_t krem) {
 }
 
 // Row keys seen by one lane: positions base + 256*s + 4*lane + c of the wave's span, read from
-// the row on every pass (the rows stay L2/MALL-resident between passes).
+// the row on every pass (the rows stay L2/MALL-resident between passes).  Loads are buffer loads
+// range-checked at round_up(n, 4) keys (the row stride is a multiple of 64 keys, so that bound
+// stays inside the row): vectors past it read as zero, keys past n inside the last vector are
+// masked, so no load sits under a branch and a batch of loads can be in flight together.
 struct Keys {
-  const uint32_t* row;
+  __amdgpu_buffer_rsrc_t rs;
   int n, base, span;
 
   __device__ void load4(int pos, uint32_t (&o)[4]) const {
-    if (pos < n) {
-      // pos is a multiple of 4 below n and the row stride a multiple of 64 keys: in the row
-      const u32x4 v = *reinterpret_cast<const u32x4*>(row + pos);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, pos * 4, 0, 0);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[c] = (pos + c < n) ? v[c] : 0u;
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) o[c] = 0u;
-    }
+    for (int c = 0; c < 4; ++c) o[c] = (pos + c < n) ? (uint32_t)v[c] : 0u;
   }
-  // f(position of c=0, keys[4]) for every `stride`-th step of the span, in order (wave-uniform)
+  // f(position of c=0, keys[4]) for every `stride`-th step of the span, in order (wave-uniform).
+  // Steps are loaded kBatch at a time before any is used.
   template <class F>
   __device__ void each(F&& f, int stride = 1) const {
+    constexpr int kBatch = 4;
     const int lane = threadIdx.x & 63;
-    for (int s = 0; 256 * s < span; s += stride) {
-      uint32_t t[4];
-      load4(base + 256 * s + 4 * lane, t);
-      f(base + 256 * s + 4 * lane, t);
+    const int steps = span >> 8;
+    for (int s = 0; s < steps; s += kBatch * stride) {
+      uint32_t t[kBatch][4];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) load4(base + 256 * (s + u * stride) + 4 * lane, t[u]);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (s + u * stride < steps) f(base + 256 * (s + u * stride) + 4 * lane, t[u]);
     }
   }
 };
@@ -289,6 +320,8 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
         n = min(max(off + (t - qb) + 1, 0), max(lk, 0));
       }
     }
+    n = __builtin_amdgcn_readfirstlane(n);  // the same for every lane: keep it scalar
+    kb = __builtin_amdgcn_readfirstlane(kb);
     const uint32_t* const row = p.keys + (int64_t)t * p.ld;
     int32_t* const oid = p.out_ids + (int64_t)t * topk;
     float* const osc = p.out_scores + (int64_t)t * topk;
@@ -306,12 +339,14 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
     }
 
     Keys ks;
-    ks.row = row;
+    ks.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(row), (short)0, ((n + 3) & ~3) * 4,
+                                              kRsrcWord3);
     ks.n = n;
     ks.span = ((n + NW * 256 - 1) / (NW * 256)) * 256;
     ks.base = wv * ks.span;
 
     // ---- A: threshold from a sample: every key of every 4th step of each wave's span --------
+    for (int i = tid; i < kHistBins; i += NT) sm.hist[i] = 0u;  // free since the last row's barriers
     uint32_t smin = 0xffffffffu, smax = 0u, scnt = 0;
     ks.each([&](int, const uint32_t (&k4)[4]) {
 #pragma unroll
@@ -325,47 +360,48 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
     smax = wave_max(smax);
     scnt = wave_sum(scnt);
     if (lane == 0) {
-      sm.wred[wv][1] = smin;
-      sm.wred[wv][2] = smax;
-      sm.wred[wv][3] = scnt;
+      sm.wred[wv][4] = smin;
+      sm.wred[wv][5] = smax;
+      sm.wred[wv][6] = scnt;
     }
     __syncthreads();
     uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-      smin = min(smin, sm.wred[i][1]);
-      smax = max(smax, sm.wred[i][2]);
-      m += sm.wred[i][3];
+      smin = min(smin, sm.wred[i][4]);
+      smax = max(smax, sm.wred[i][5]);
+      m += sm.wred[i][6];
     }
     smin += 1u;
     // sample rank whose bin edge becomes theta: k*m/n plus 4 standard deviations and a margin
     const float expect = (float)topk * (float)m / (float)n;
     const uint32_t r = (uint32_t)(expect + 4.f * __builtin_sqrtf(expect) + 8.f);
     uint32_t theta = 1u;  // every real key is >= 0x007fffff
-    __syncthreads();
     if (m >= 64 && r < m && smax > smin) {
       const uint32_t srange = smax - smin;
       const int sbits = 32 - __clz((int)srange);
       const int sshift = max(sbits - kHistBits, 0);
-      for (int i = tid; i < kHistBins; i += NT) sm.hist[i] = 0u;
-      __syncthreads();
       ks.each([&](int, const uint32_t (&k4)[4]) {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
           if (k4[c]) atomicAdd(&sm.hist[(k4[c] - smin) >> sshift], 1u);
       }, kSampleStride);
       __syncthreads();
-      find_bin<NT>(sm, kHistBins, r);
+      find_bin<NT>(sm, kHistBins, r);  // ends with a barrier: the histogram is free afterwards
       theta = smin + (sm.bcast[0] << sshift);
-      __syncthreads();
     }
 
     // ---- B: keys >= theta into this wave's region, in position order ---------------------------
-    uint32_t run = 0;
+    // the histogram is free again: clear it for the first digit pass over the survivors
+    for (int i = tid; i < kHistBins; i += NT) sm.hist[i] = 0u;
+    uint32_t run = 0, rmax = 0;
     ks.each([&](int pos, const uint32_t (&k4)[4]) {
       uint32_t cnt = 0;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) cnt += k4[c] >= theta ? 1u : 0u;
+      for (int c = 0; c < 4; ++c) {
+        cnt += k4[c] >= theta ? 1u : 0u;
+        rmax = max(rmax, k4[c]);
+      }
       uint32_t ex, tot;
       wave_prefix3(cnt, ex, tot);
       if (tot) {
@@ -383,39 +419,39 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
       }
       run += tot;
     });
-    if (lane == 0) sm.wred[wv][1] = run;
+    rmax = wave_max(rmax);
+    if (lane == 0) {
+      sm.wred[wv][7] = run;
+      sm.wred[wv][8] = rmax;
+    }
+    if (tid == 0) sm.bcast[3] = 0u;  // gather counter of the direct ranking below
     __syncthreads();
-    uint32_t total = 0;
+    uint32_t total = 0, cmax = 0;
     bool overflow = false;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-      total += sm.wred[i][1];
-      overflow |= sm.wred[i][1] > (uint32_t)R;
+      total += sm.wred[i][7];
+      cmax = max(cmax, sm.wred[i][8]);
+      overflow |= sm.wred[i][7] > (uint32_t)R;
     }
     const uint32_t mine = min(run, (uint32_t)R);
-    __syncthreads();
 
     uint32_t T, eq_skip, sel_base, eq_base;
     if (!overflow && total >= (uint32_t)topk) {
       // ---- C: exact k-th key among the survivors ---------------------------------------------
-      uint32_t cmax = 0;
-      for (uint32_t i = lane; i < mine; i += 64) cmax = max(cmax, sm.ckey[wv][i]);
-      cmax = wave_max(cmax);
-      if (lane == 0) sm.wred[wv][2] = cmax;
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < NW; ++i) cmax = max(cmax, sm.wred[i][2]);
+      // cmax (the row maximum) is a survivor, so [theta, cmax] spans every survivor
       const uint32_t range = cmax - theta;
       int shift = range ? 32 - __clz((int)range) : 0;
       uint32_t prefix = 0, krem = (uint32_t)topk, eq_total = total;
       bool first = true;
-      __syncthreads();
       while (shift > 0) {
         const int bits = min(kHistBits, shift);
         shift -= bits;
         const uint32_t nb = 1u << bits;
-        for (int i = tid; i < (int)nb; i += NT) sm.hist[i] = 0u;
-        __syncthreads();
+        if (!first) {  // the first pass uses the histogram cleared during compaction
+          for (int i = tid; i < (int)nb; i += NT) sm.hist[i] = 0u;
+          __syncthreads();
+        }
         for (uint32_t i = lane; i < mine; i += 64) {
           const uint32_t v = sm.ckey[wv][i] - theta;
           if (first || (uint32_t)((uint64_t)v >> (shift + bits)) == prefix)
@@ -427,12 +463,9 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
         krem -= sm.bcast[1];
         eq_total = sm.bcast[2];
         first = false;
-        __syncthreads();
         if (shift > 0 && eq_total <= 64u) {
           // Few keys left in the bin: rank them directly.  Gather them (any order) and let lane
           // i of wave 0 count how many are greater / greater-or-equal than key i.
-          if (tid == 0) sm.bcast[3] = 0u;
-          __syncthreads();
           for (uint32_t i = lane; i < mine; i += 64) {
             const uint32_t kk = sm.ckey[wv][i];
             if (((kk - theta) >> shift) == prefix) sm.hist[atomicAdd(&sm.bcast[3], 1u)] = kk;
@@ -443,7 +476,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
             const uint32_t mykey = (uint32_t)lane < c ? sm.hist[lane] : 0u;
             uint32_t gt = 0, ge = 0;
             for (uint32_t j = 0; j < c; ++j) {
-              const uint32_t o = sm.hist[j];
+              const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mykey, (int)j);
               gt += o > mykey ? 1u : 0u;
               ge += o >= mykey ? 1u : 0u;
             }
@@ -458,7 +491,6 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
           krem -= sm.bcast[5];
           eq_total = sm.bcast[6];
           shift = 0;
-          __syncthreads();
         }
       }
       T = theta + prefix;
@@ -536,7 +568,6 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
         sel_run += sel_tot;
       });
     }
-    __syncthreads();  // LDS is reused by the next row
   }
 }
 
