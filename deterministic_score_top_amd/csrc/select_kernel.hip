@@ -13,7 +13,7 @@
 //   B  one pass compares every key with theta and copies the survivors (key, position) into
 //      per-wave LDS regions in position order (ballots + mbcnt, no atomics);
 //   C  the exact k-th key T is found over the survivors with range-normalised LDS histograms
-//      (11, 11, 10 bits), together with how many keys equal T and how many of those are left
+//      (digits of up to 10 bits), together with how many keys equal T and how many of those are left
 //      out (the lowest positions);
 //   D  the survivors are written in position order: wave w starts at the fixed-order sum of
 //      the selected counts of waves 0..w-1, lanes are ranked with ballots and mbcnt.
@@ -31,7 +31,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kHistBits = 11;
+constexpr int kHistBits = 10;
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kCandCap = 3072;    // survivors per row held in LDS
 constexpr int kSegCache = 256;    // segments whose tables are cached in LDS
