@@ -105,6 +105,7 @@ template <int NT>
 struct alignas(16) Smem {
   static constexpr int NW = NT / 64;
   static constexpr int R = kCandCap / NW;  // survivors per wave region
+  static_assert(R % 256 == 0, "wave regions are read in steps of 256 entries");
   uint32_t hist[kHistBins];
   uint32_t ckey[NW][R];
   uint16_t cpos[NW][R];
@@ -435,6 +436,13 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
       overflow |= sm.wred[i][7] > (uint32_t)R;
     }
     const uint32_t mine = min(run, (uint32_t)R);
+    // entries i0 + 64c + lane (c = 0..3) of this wave's region, all four read before any is
+    // used; the region holds a whole number of 256-entry steps, so the reads stay inside it
+    // (entries at or past `mine` are stale and masked by the callers)
+    auto cand4 = [&](uint32_t i0, uint32_t (&kk)[4]) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kk[c] = sm.ckey[wv][i0 + 64 * c + lane];
+    };
 
     uint32_t T, eq_skip, sel_base, eq_base;
     if (!overflow && total >= (uint32_t)topk) {
@@ -452,10 +460,15 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
           for (int i = tid; i < (int)nb; i += NT) sm.hist[i] = 0u;
           __syncthreads();
         }
-        for (uint32_t i = lane; i < mine; i += 64) {
-          const uint32_t v = sm.ckey[wv][i] - theta;
-          if (first || (uint32_t)((uint64_t)v >> (shift + bits)) == prefix)
-            atomicAdd(&sm.hist[(v >> shift) & (nb - 1u)], 1u);
+        for (uint32_t i0 = 0; i0 < mine; i0 += 256) {
+          uint32_t kk[4];
+          cand4(i0, kk);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t v = kk[c] - theta;
+            if (i0 + 64 * c + lane < mine && (first || (uint32_t)((uint64_t)v >> (shift + bits)) == prefix))
+              atomicAdd(&sm.hist[(v >> shift) & (nb - 1u)], 1u);
+          }
         }
         __syncthreads();
         find_bin<NT>(sm, (int)nb, krem);
@@ -466,9 +479,13 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
         if (shift > 0 && eq_total <= 64u) {
           // Few keys left in the bin: rank them directly.  Gather them (any order) and let lane
           // i of wave 0 count how many are greater / greater-or-equal than key i.
-          for (uint32_t i = lane; i < mine; i += 64) {
-            const uint32_t kk = sm.ckey[wv][i];
-            if (((kk - theta) >> shift) == prefix) sm.hist[atomicAdd(&sm.bcast[3], 1u)] = kk;
+          for (uint32_t i0 = 0; i0 < mine; i0 += 256) {
+            uint32_t kk[4];
+            cand4(i0, kk);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if (i0 + 64 * c + lane < mine && ((kk[c] - theta) >> shift) == prefix)
+                sm.hist[atomicAdd(&sm.bcast[3], 1u)] = kk[c];
           }
           __syncthreads();
           if (wv == 0) {
@@ -496,10 +513,15 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
       T = theta + prefix;
       eq_skip = eq_total - krem;
       uint32_t gt = 0, eq = 0;
-      for (uint32_t i = lane; i < mine; i += 64) {
-        const uint32_t kk = sm.ckey[wv][i];
-        gt += kk > T ? 1u : 0u;
-        eq += kk == T ? 1u : 0u;
+      for (uint32_t i0 = 0; i0 < mine; i0 += 256) {
+        uint32_t kk[4];
+        cand4(i0, kk);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const bool live = i0 + 64 * c + lane < mine;
+          gt += live && kk[c] > T ? 1u : 0u;
+          eq += live && kk[c] == T ? 1u : 0u;
+        }
       }
       gt = wave_sum(gt);
       eq = wave_sum(eq);
@@ -511,22 +533,28 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
       wave_bases<NT>(sm, eq_skip, sel_base, eq_base);
       // ---- D: ordered write from the survivors ------------------------------------------------
       uint32_t eq_run = eq_base, sel_run = sel_base;
-      for (uint32_t i0 = 0; i0 < mine; i0 += 64) {
-        const uint32_t i = i0 + lane;
-        const bool live = i < mine;
-        const uint32_t kk = live ? sm.ckey[wv][i] : 0u;
-        const bool eqf = live && kk == T;
-        const bool gtf = live && kk > T;
-        const uint64_t eqm = __ballot(eqf);
-        const bool self = gtf || (eqf && eq_run + lanes_below(eqm) >= eq_skip);
-        const uint64_t selm = __ballot(self);
-        const uint32_t slot = sel_run + lanes_below(selm);
-        if (self && slot < (uint32_t)topk) {  // exactly topk are selected; the bound is a guard
-          oid[slot] = kb + (int)sm.cpos[wv][i];
-          osc[slot] = key_value(kk);
+      for (uint32_t i0 = 0; i0 < mine; i0 += 256) {
+        uint32_t kk[4];
+        int pos[4];
+        cand4(i0, kk);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) pos[c] = sm.cpos[wv][i0 + 64 * c + lane];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {  // entries i0 + 64c + lane: region order
+          const bool live = i0 + 64 * c + lane < mine;
+          const bool eqf = live && kk[c] == T;
+          const bool gtf = live && kk[c] > T;
+          const uint64_t eqm = __ballot(eqf);
+          const bool self = gtf || (eqf && eq_run + lanes_below(eqm) >= eq_skip);
+          const uint64_t selm = __ballot(self);
+          const uint32_t slot = sel_run + lanes_below(selm);
+          if (self && slot < (uint32_t)topk) {  // exactly topk are selected; the bound is a guard
+            oid[slot] = kb + pos[c];
+            osc[slot] = key_value(kk[c]);
+          }
+          eq_run += (uint32_t)__popcll(eqm);
+          sel_run += (uint32_t)__popcll(selm);
         }
-        eq_run += (uint32_t)__popcll(eqm);
-        sel_run += (uint32_t)__popcll(selm);
       }
     } else {
       // ---- exact fallback over every key ------------------------------------------------------
