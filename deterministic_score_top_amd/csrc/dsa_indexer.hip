@@ -102,7 +102,8 @@ int launch_scores(const Call& c, hipStream_t stream) {
   if (c.tuning) {
     if (c.tuning->grid_blocks < 0 || c.tuning->key_chunk_tiles < 0) return DSA_ERR_SHAPE;
     if (c.tuning->grid_blocks > 0) grid = c.tuning->grid_blocks;
-    chunk = c.tuning->key_chunk_tiles;
+    // the knob counts 64-key tiles; units hold whole kernel tiles
+    chunk = (int)(((int64_t)c.tuning->key_chunk_tiles * 64 + dsa::kTileKeys - 1) / dsa::kTileKeys);
   }
   if (chunk == 0) {
     // Units should be few (each start reloads the query block) but numerous enough to balance:

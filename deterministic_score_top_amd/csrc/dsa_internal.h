@@ -15,7 +15,10 @@ constexpr int kDim = 128;        // head dim D
 constexpr int kScoreThreads = DSA_SCORE_THREADS;  // one query per wave
 constexpr int kWaves = kScoreThreads / 64;
 constexpr int kTileQueries = kWaves;                     // one query per wave; queries per unit
-constexpr int kTileKeys = 64;                            // keys per LDS stage
+#ifndef DSA_TILE_KEYS
+#define DSA_TILE_KEYS 64
+#endif
+constexpr int kTileKeys = DSA_TILE_KEYS;                 // keys per LDS stage (64 or 128)
 constexpr int kCtrlBytes = 256;                          // control block at workspace offset 0
 constexpr int kMaxTopk = 2048;
 constexpr int kMaxSeqlenK = 65536;

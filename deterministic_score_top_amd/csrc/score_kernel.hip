@@ -40,6 +40,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kKBufBytes = kTileKeys * kDim * 2;  // one staged key tile: 16 KiB
+constexpr int kKBufs = 3;                         // LDS tile buffers: tiles land two ahead
+// s_waitcnt immediate that waits only on the vector memory counter: OR in the count (< 16);
+// expcnt (bits 6:4) and lgkmcnt (bits 11:8) at their maxima do not wait
+constexpr int kWaitVm = 0x0F70;
 constexpr int kSlotInts = 16;
 constexpr int kPartEntries = kScoreThreads + 4;
 // Buffer resource word 3 for raw (stride 0) 32-bit buffers on gfx9-family parts, and a byte
@@ -127,7 +131,8 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* const kbuf0 = smem;
   unsigned char* const kbuf1 = smem + kKBufBytes;
-  int* const slot = reinterpret_cast<int*>(smem + 2 * kKBufBytes);
+  unsigned char* const kbuf2 = smem + 2 * kKBufBytes;
+  int* const slot = reinterpret_cast<int*>(smem + kKBufs * kKBufBytes);
   uint32_t* const part = reinterpret_cast<uint32_t*>(slot + kSlotInts);
   uint32_t* const seg_tp = part + kPartEntries;                   // B + 1 entries
   uint32_t* const unit_pf = seg_tp + ((p.B + 1 + 3) & ~3);        // max_tiles + 1 entries
@@ -272,22 +277,19 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
     // operations.
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(p.k + (int64_t)kb * kDim), (short)0, lk * (kDim * 2), kRsrcWord3);
-    uint4 kregA[kStageChunks], kregB[kStageChunks];
-    auto gload = [&](uint4 (&kr)[kStageChunks], int kt0) {
+    // A tile is written to LDS by buffer loads that deposit each lane's 16 bytes directly at
+    // LDS base + 16 * lane (no register staging).  Instruction r of wave wv fills the 1 KiB
+    // block id = r * kWaves + wv, i.e. key rows 4*id .. 4*id+3; lane l writes chunk position
+    // l & 15 of row 4*id + (l >> 4), so it fetches the global 16-byte chunk that the XOR
+    // swizzle maps there.
+    auto ldsload = [&](unsigned char* buf, int kt0) {
 #pragma unroll
       for (int r = 0; r < kStageChunks; ++r) {
-        const int id = r * kScoreThreads + tid;
-        const int s = id >> 4, cc = id & 15;
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(krs, (kt0 + s) * (kDim * 2) + cc * 16, 0, 0);
-        kr[r] = make_uint4(v[0], v[1], v[2], v[3]);
-      }
-    };
-    auto swrite = [&](const uint4 (&kr)[kStageChunks], unsigned char* buf) {
-#pragma unroll
-      for (int r = 0; r < kStageChunks; ++r) {
-        const int id = r * kScoreThreads + tid;
-        const int s = id >> 4, cc = id & 15;
-        *reinterpret_cast<uint4*>(buf + s * (kDim * 2) + ((cc ^ (s & 15)) << 4)) = kr[r];
+        const int id = r * kWaves + wv;
+        const int s = 4 * id + (lane >> 4), pos = lane & 15;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            krs, (__attribute__((address_space(3))) void*)(buf + id * 1024), 16,
+            (kt0 + s) * (kDim * 2) + ((pos ^ (s & 15)) << 4), 0, 0, 0);
       }
     };
     // One phase = the MFMAs of one 32-key column block (2 row blocks x 8 K-steps) into (n0, n1),
@@ -317,54 +319,72 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
       }
       return half_swap_sum(p0 + p1);
     };
-    // scores of a tile are stored after the barrier that follows it, so the store latency is
-    // covered by the next tile's work instead of by the wait before the next LDS tile write
-    // scores of (previous tile, column block 1) and (this tile, column block 0); a negative
-    // previous tile start means there is none and its store is dropped
+    // Scores of a tile are stored after the barrier that follows it, so the store latency is
+    // covered by the next tile's work instead of by the wait before the next LDS tile write.
+    // Column block cb of a tile computes its MFMAs while finishing the epilogue of the block
+    // before it: sc[0] is the last block of the previous tile (none when kt_prev < 0: its
+    // store is dropped), sc[cb] for cb >= 1 is block cb-1 of this tile.  Accumulator pairs
+    // alternate: even blocks in c0, odd blocks in c1.
     const bool keys_out = p.store_keys != 0;
     auto outbits = [&](float v) -> uint32_t { return keys_out ? score_key(v) : __float_as_uint(v); };
-    auto store = [&](float s_prev, int kt_prev, float s_cur, int kt_cur) {
-      const int kp = kt_prev + 32 + n, kc = kt_cur + n;
-      __builtin_amdgcn_raw_buffer_store_b32(outbits(s_prev), ors,
-                                            (hf == 0 && kt_prev >= 0) ? kp * 4 : kDropOffset, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(outbits(s_cur), ors, hf == 0 ? kc * 4 : kDropOffset, 0, 0);
+    constexpr int kPhases = kTileKeys / 32;
+    static_assert(kPhases % 2 == 0, "column blocks alternate between two accumulator pairs");
+    f32x16 c0a, c0b, c1a = f32x16{}, c1b = f32x16{};
+    auto tile = [&](const unsigned char* buf, float (&sc)[kPhases]) {
+#pragma unroll
+      for (int cb = 0; cb < kPhases; ++cb)
+        sc[cb] = (cb & 1) ? phase(buf, cb, c1a, c1b, c0a, c0b) : phase(buf, cb, c0a, c0b, c1a, c1b);
+    };
+    auto store_tile = [&](const float (&sc)[kPhases], int kt_prev, int kt0) {
+      __builtin_amdgcn_raw_buffer_store_b32(
+          outbits(sc[0]), ors, (hf == 0 && kt_prev >= 0) ? (kt_prev + 32 * (kPhases - 1) + n) * 4 : kDropOffset,
+          0, 0);
+#pragma unroll
+      for (int cb = 1; cb < kPhases; ++cb)
+        __builtin_amdgcn_raw_buffer_store_b32(outbits(sc[cb]), ors,
+                                              hf == 0 ? (kt0 + 32 * (cb - 1) + n) * 4 : kDropOffset, 0, 0);
     };
 
     const int ntl = kend > kbeg ? ceil_div(kend - kbeg, kTileKeys) : 0;
-    if (ntl > 0) gload(kregA, kbeg);
-    if (ntl > 1) gload(kregB, kbeg + kTileKeys);
-    if (ntl > 0) swrite(kregA, kbuf0);
+    if (ntl > 0) ldsload(kbuf0, kbeg);
+    if (ntl > 1) ldsload(kbuf1, kbeg + kTileKeys);
     // Everything loaded before the tile loop (query block, weights, first tiles) has landed
     // here; saying so once keeps per-use waits on the query registers out of the loop, where
     // they would also wait for the prefetched tiles and the score stores.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // c0*: column block 0 of the current tile; c1*: column block 1 (of the previous tile while
-    // the current tile's block 0 is multiplied)
-    f32x16 c0a, c0b, c1a = f32x16{}, c1b = f32x16{};
     int kt_prev = -1;
-    for (int tt = 0; tt < ntl; tt += 2) {
-      int kt0 = kbeg + tt * kTileKeys;
-      // tile tt is in kbuf0, tile tt+1 is in flight in kregB, kregA is free
-      if (tt + 2 < ntl) gload(kregA, kt0 + 2 * kTileKeys);
-      float s_prev = phase(kbuf0, 0, c0a, c0b, c1a, c1b);
-      float s_cur = phase(kbuf0, 1, c1a, c1b, c0a, c0b);
-      if (tt + 1 < ntl) swrite(kregB, kbuf1);
-      __syncthreads();
-      store(s_prev, kt_prev, s_cur, kt0);
+    float sc[kPhases];
+    // One tile: tile t+2 starts loading into the buffer that tile t-1 used (free since the
+    // barrier after it), tile t is multiplied, then this wave waits until its part of tile t+1
+    // is in LDS, and the barrier makes all of tile t+1 visible.  Vector memory operations
+    // complete in issue order; after tile t+1's loads this wave has issued tile t-1's score
+    // stores (kPhases) and, when present, tile t+2's loads (kStageChunks), so waiting until at
+    // most that many are outstanding covers tile t+1.
+    auto step = [&](unsigned char* cur, unsigned char* next2, int t) {
+      const int kt0 = kbeg + t * kTileKeys;
+      if (t + 2 < ntl) ldsload(next2, kt0 + 2 * kTileKeys);
+      tile(cur, sc);
+      if (t + 2 < ntl) {
+        __builtin_amdgcn_s_waitcnt(kWaitVm | (kPhases + kStageChunks));
+      } else {
+        __builtin_amdgcn_s_waitcnt(kWaitVm | kPhases);
+      }
+      // A plain barrier: a fenced one would also wait for tile t+2's loads.  The memory
+      // clobber keeps the compiler from moving LDS accesses across it; this wave's reads of
+      // tile t are complete (their MFMAs have issued), and its part of tile t+1 has landed.
+      asm volatile("s_barrier" ::: "memory");
+      store_tile(sc, kt_prev, kt0);
       kt_prev = kt0;
+    };
+    for (int tt = 0; tt < ntl; tt += 3) {
+      step(kbuf0, kbuf2, tt);
       if (tt + 1 >= ntl) break;
-      // tile tt+1 is in kbuf1, tile tt+2 is in flight in kregA, kregB is free
-      kt0 += kTileKeys;
-      if (tt + 3 < ntl) gload(kregB, kt0 + 2 * kTileKeys);
-      s_prev = phase(kbuf1, 0, c0a, c0b, c1a, c1b);
-      s_cur = phase(kbuf1, 1, c1a, c1b, c0a, c0b);
-      if (tt + 2 < ntl) swrite(kregA, kbuf0);
-      __syncthreads();
-      store(s_prev, kt_prev, s_cur, kt0);
-      kt_prev = kt0;
+      step(kbuf1, kbuf0, tt + 1);
+      if (tt + 2 >= ntl) break;
+      step(kbuf2, kbuf1, tt + 2);
     }
-    if (ntl > 0) {  // column block 1 of the last tile
+    if (ntl > 0) {  // last column block of the last tile
       float p0 = 0.f, p1 = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -373,7 +393,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
       }
       const float s_last = half_swap_sum(p0 + p1);
       __builtin_amdgcn_raw_buffer_store_b32(outbits(s_last), ors,
-                                            hf == 0 ? (kt_prev + 32 + n) * 4 : kDropOffset, 0, 0);
+                                            hf == 0 ? (kt_prev + 32 * (kPhases - 1) + n) * 4 : kDropOffset, 0, 0);
     }
     u = (uint32_t)slot[4 + (iter & 1)];
     ++iter;
@@ -399,11 +419,11 @@ __global__ void ctrl_init_kernel(uint32_t* ctrl) {
 }  // namespace
 
 size_t score_smem_bytes(int B, int max_tiles) {
-  return (size_t)2 * kKBufBytes + kSlotInts * 4 + kPartEntries * 4 +
+  return (size_t)kKBufs * kKBufBytes + kSlotInts * 4 + kPartEntries * 4 +
          (size_t)((B + 1 + 3) & ~3) * 4 + (size_t)(max_tiles + 1) * 4;
 }
 
-size_t score_smem_limit() { return 80 * 1024; }
+size_t score_smem_limit() { return 144 * 1024; }
 
 hipError_t score_prepare(size_t max_smem) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel),
