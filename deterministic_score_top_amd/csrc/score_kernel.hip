@@ -308,14 +308,20 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
       for (int j = 0; j < 8; ++j) {
         const bf16x8 kf =
             *reinterpret_cast<const bf16x8*>(cur + s * (kDim * 2) + (((2 * j + hf) ^ (n & 15)) << 4));
+        // each MFMA is followed by the epilogue step of the matching row block of the previous
+        // column block (whose chain finished at least one MFMA earlier); the schedule groups
+        // keep the compiler from bunching the epilogue at the start of the phase
         n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][j], kf, n0, 0, 0, 0);
+        p0 = __builtin_fmaf(wr[2 * j], relu_bits(e0[2 * j]), p0);
+        p0 = __builtin_fmaf(wr[2 * j + 1], relu_bits(e0[2 * j + 1]), p0);
         n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][j], kf, n1, 0, 0, 0);
-#pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-          const int i = 2 * j + ii;
-          p0 = __builtin_fmaf(wr[i], relu_bits(e0[i]), p0);
-          p1 = __builtin_fmaf(wr[16 + i], relu_bits(e1[i]), p1);
-        }
+        p1 = __builtin_fmaf(wr[16 + 2 * j], relu_bits(e1[2 * j]), p1);
+        p1 = __builtin_fmaf(wr[16 + 2 * j + 1], relu_bits(e1[2 * j + 1]), p1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
       }
       return half_swap_sum(p0 + p1);
     };
