@@ -239,3 +239,39 @@ def test_full_config_sampled(name):
                 if i >= 0:
                     groups.setdefault(kb[i].tobytes(), set()).add(float(s))
             assert all(len(v) == 1 for v in groups.values())
+
+
+def test_weight_power_of_two_scaling_bitwise():
+    # w x 2^j scales every FP32 partial sum by 2^j exactly: scores scale bit-exactly, ids are unchanged
+    wl = W.random_segments([40, 9, 77], [300, 50, 1000], [200, 0, 900], topk=64, seed=40)
+    q, k, w, cq, ck, offs = _dev(wl)
+    base = _run(wl, (q, k, w, cq, ck, offs))
+    for j in (-3, 2, 5):
+        ids, sc = _run(wl, (q, k, w * (2.0 ** j), cq, ck, offs))
+        assert np.array_equal(ids, base[0])
+        live = base[0] >= 0
+        assert np.array_equal(sc[live], (base[1][live].astype(np.float64) * 2.0 ** j).astype(np.float32))
+
+
+def test_cp_tail_rows_equal_full_document_rows():
+    # the context-parallel tail (queries 61440..65535 of a 65536-key document) returns exactly the
+    # rows of the same queries in one causal call over the whole document
+    tail = W.make("cp_tail")
+    n, nq = tail.Tkv, tail.T
+    d = "cuda"
+    g = torch.Generator(device=d).manual_seed(7)
+    q_full = torch.randn((n, 64, 128), generator=g, device=d).to(torch.bfloat16)
+    w_full = torch.rand((n, 64), generator=g, device=d) / 8
+    q_full[n - nq:] = tail.q.to(d)
+    w_full[n - nq:] = tail.w.to(d)
+    k = tail.k.to(d)
+    cu = torch.tensor([0, n], dtype=torch.int32, device=d)
+    ws = ix.alloc_workspace(n, n, 1, n, d)   # 17 GB of score rows, freed below
+    ids_f, sc_f = ix.topk(q_full, k, w_full, cu, cu, None, topk=tail.topk, workspace=ws, max_seqlen_k=n)
+    torch.cuda.synchronize()
+    ids_f, sc_f = ids_f[n - nq:].cpu().numpy(), sc_f[n - nq:].cpu().numpy()
+    del q_full, w_full, ws
+    torch.cuda.empty_cache()
+    ids_t, sc_t = _run(tail)
+    assert np.array_equal(ids_f, ids_t)
+    assert np.array_equal(sc_f.view(np.uint32), sc_t.view(np.uint32))
