@@ -129,9 +129,17 @@ def cpu_baseline(wl, ids, sc, budget_s):
         ok = False
         print(f"bench: sampled parity FAILED: {e}", file=sys.stderr)
     what = "all" if len(done) == wl.T else "a seeded random sample of"
+    cpu = "unknown cpu"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                cpu = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": len(done) / el, "unit": "queries/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": f"{what} {len(done)} of {wl.T} query rows of the same workload, one oracle call per row, "
-                      f"{el:.1f} s, FP64 NumPy, host cpu_count={os.cpu_count()}"}, ok
+                      f"{el:.1f} s, FP64 NumPy, host cpu_count={os.cpu_count()} ({cpu})"}, ok
 
 
 def main():
@@ -142,6 +150,13 @@ def main():
     ap.add_argument("--config", default="causal_n8192")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hold-cus", type=int, default=0,
+                    help="before each timed call, hold this many CUs with a foreign kernel (tests/native "
+                         "helper) for --hold-frac of the warm call time")
+    ap.add_argument("--hold-frac", type=float, default=0.5)
+    ap.add_argument("--cold", action="store_true",
+                    help="overwrite a 512 MiB buffer between timed calls (L2 and MALL cold); value is then "
+                         "T / median per-call GPU time")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of known size (counter calibration)")
     ap.add_argument("--ingest-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -174,24 +189,52 @@ def main():
     out_sc = torch.empty((wl.T, wl.topk), dtype=torch.float32, device=dev)
     call = dict(topk=wl.topk, workspace=ws, max_seqlen_k=wl.max_seqlen_k, out_ids=out_ids, out_scores=out_sc)
 
+    flush = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev) if args.cold else None
     for _ in range(args.warmup):
         ix.topk(q, k, w, cq, ck, offs, **call)
     torch.cuda.synchronize()
+    hold = None
+    if args.hold_cus > 0:
+        import ctypes
+        hold = ctypes.CDLL(os.path.join(ROOT, "tests", "native", "libspinner.so"))
+        hold.spinner_start.argtypes = [ctypes.c_int, ctypes.c_double]
+        hold.spinner_wait_resident.argtypes = [ctypes.c_double]
+        wprof = ix.Profiler(20)
+        for _ in range(20):
+            ix.topk(q, k, w, cq, ck, offs, profiler=wprof, **call)
+        a, b = wprof.read_calls()
+        wprof.close()
+        hold_us = args.hold_frac * 1000.0 * sorted(x + y for x, y in zip(a, b))[len(a) // 2]
+        args.steps = min(args.steps, 50)
     prof = ix.Profiler(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
+        if flush is not None:
+            flush.fill_(1.0)
+        if hold is not None:
+            torch.cuda.synchronize()
+            if hold.spinner_start(args.hold_cus, hold_us) != 0 or hold.spinner_wait_resident(1000.0) != 0:
+                raise SystemExit("bench: could not start the CU holder")
         ix.topk(q, k, w, cq, ck, offs, profiler=prof, **call)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
-    score_ms, select_ms, calls = prof.read()
+    per_score, per_select = prof.read_calls()
     prof.close()
+    calls = len(per_score)
+    score_ms, select_ms = sum(per_score), sum(per_select)
+    per_call = sorted(a + b for a, b in zip(per_score, per_select))
+
+    def pct(v, f):
+        return v[min(len(v) - 1, int(round(f * (len(v) - 1))))]
     st = ix.read_status(ws)
     if st != (0, 0, 0):
         print(f"bench: workspace status {st}", file=sys.stderr)
 
     pairs = visible_pairs(wl)
     ms = el * 1000.0 / args.steps
+    if args.cold or hold is not None:   # time the calls themselves on the GPU
+        ms = pct(per_call, 0.5)
     score_avg_ms = score_ms / calls
     select_avg_ms = select_ms / calls
     eff_call = FLOP_PER_PAIR * pairs / (ms * 1e-3) / 1e12
@@ -219,6 +262,11 @@ def main():
         "frac_bf16_peak_call": eff_call / PEAK_BF16_TFLOPS,
         "score_kernel_ms": score_avg_ms,
         "select_kernel_ms": select_avg_ms,
+        "call_gpu_ms": {"p10": pct(per_call, 0.1), "p50": pct(per_call, 0.5), "p90": pct(per_call, 0.9),
+                        "l2": "cold (512 MiB written between calls)" if args.cold else "warm"},
+        "foreign_load": ({"held_cus": args.hold_cus, "held_us": hold_us,
+                          "note": "a foreign kernel holds the CUs from just before each call for that long"}
+                         if hold is not None else None),
         "roofline": {"bound": "mfma", "kernel": "score_kernel", "achieved": eff_score,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": eff_score / PEAK_BF16_TFLOPS,
                      "traffic": load_traffic(args.config)},

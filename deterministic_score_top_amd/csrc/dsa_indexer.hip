@@ -287,6 +287,21 @@ int dsa_indexer_profiler_destroy(dsa_indexer_profiler* prof) {
   return DSA_OK;
 }
 
+int dsa_indexer_profiler_read_calls(dsa_indexer_profiler* prof, float* score_ms, float* select_ms,
+                                    int32_t max_calls, int32_t* calls) {
+  if (!prof || !score_ms || !select_ms || !calls) return DSA_ERR_NULL;
+  if (prof->used > max_calls) return DSA_ERR_SHAPE;
+  for (int i = 0; i < prof->used; ++i) {
+    hipEvent_t* e = &prof->ev[3 * i];
+    if (hipEventSynchronize(e[2]) != hipSuccess) return DSA_ERR_LAUNCH;
+    if (hipEventElapsedTime(&score_ms[i], e[0], e[1]) != hipSuccess) return DSA_ERR_LAUNCH;
+    if (hipEventElapsedTime(&select_ms[i], e[1], e[2]) != hipSuccess) return DSA_ERR_LAUNCH;
+  }
+  *calls = prof->used;
+  prof->used = 0;
+  return DSA_OK;
+}
+
 int dsa_indexer_profiler_read(dsa_indexer_profiler* prof, double* score_ms, double* select_ms,
                               int32_t* calls) {
   if (!prof || !score_ms || !select_ms || !calls) return DSA_ERR_NULL;

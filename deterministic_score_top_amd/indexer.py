@@ -37,6 +37,7 @@ EXPORTED_SYMBOLS = (
     "dsa_indexer_profiler_create",
     "dsa_indexer_profiler_destroy",
     "dsa_indexer_profiler_read",
+    "dsa_indexer_profiler_read_calls",
     "dsa_indexer_topk_ex",
     "dsa_indexer_read_status",
 )
@@ -93,6 +94,9 @@ def lib():
         L.dsa_indexer_profiler_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
                                                 ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
         L.dsa_indexer_profiler_read.restype = ctypes.c_int
+        L.dsa_indexer_profiler_read_calls.argtypes = [vp, ctypes.POINTER(ctypes.c_float),
+                                                      ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32)]
+        L.dsa_indexer_profiler_read_calls.restype = ctypes.c_int
         L.dsa_indexer_read_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32),
                                               ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32)]
         L.dsa_indexer_read_status.restype = ctypes.c_int
@@ -172,12 +176,22 @@ class Profiler:
         h = ctypes.c_void_p()
         _check(lib().dsa_indexer_profiler_create(int(capacity), ctypes.byref(h)), "profiler_create")
         self.handle = h
+        self.capacity = int(capacity)
 
     def read(self):
         a, b, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int32()
         _check(lib().dsa_indexer_profiler_read(self.handle, ctypes.byref(a), ctypes.byref(b), ctypes.byref(n)),
                "profiler_read")
         return a.value, b.value, n.value
+
+    def read_calls(self):
+        """Per-call (score ms, select ms) lists, oldest first; empties the profiler."""
+        a = (ctypes.c_float * self.capacity)()
+        b = (ctypes.c_float * self.capacity)()
+        n = ctypes.c_int32()
+        _check(lib().dsa_indexer_profiler_read_calls(self.handle, a, b, self.capacity, ctypes.byref(n)),
+               "profiler_read_calls")
+        return list(a[:n.value]), list(b[:n.value])
 
     def close(self):
         if self.handle:

@@ -154,6 +154,14 @@ int dsa_indexer_profiler_create(int32_t capacity, dsa_indexer_profiler** out);
 int dsa_indexer_profiler_destroy(dsa_indexer_profiler* prof);
 int dsa_indexer_profiler_read(dsa_indexer_profiler* prof, double* score_ms, double* select_ms,
                               int32_t* calls);
+/*
+ * Per-call form of dsa_indexer_profiler_read: synchronises, writes the score-kernel and
+ * select-kernel milliseconds of each recorded call (oldest first) to score_ms[i] and
+ * select_ms[i] for i < *calls (host arrays of `max_calls` floats; DSA_ERR_SHAPE if the
+ * profiler holds more calls than that), and empties the slots.
+ */
+int dsa_indexer_profiler_read_calls(dsa_indexer_profiler* prof, float* score_ms, float* select_ms,
+                                    int32_t max_calls, int32_t* calls);
 
 /* dsa_indexer_topk with optional tuning (NULL = defaults) and optional profiler (NULL = none). */
 int dsa_indexer_topk_ex(const dsa_indexer_shape* shape, const void* q, const void* k,

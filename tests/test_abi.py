@@ -100,3 +100,4 @@ def test_profiler_argument_errors():
     h = ctypes.c_void_p()
     assert L.dsa_indexer_profiler_create(0, ctypes.byref(h)) == -3
     assert L.dsa_indexer_profiler_read(None, None, None, None) == -1
+    assert L.dsa_indexer_profiler_read_calls(None, None, None, 0, None) == -1

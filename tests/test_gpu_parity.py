@@ -275,3 +275,33 @@ def test_cp_tail_rows_equal_full_document_rows():
     ids_t, sc_t = _run(tail)
     assert np.array_equal(ids_f, ids_t)
     assert np.array_equal(sc_f.view(np.uint32), sc_t.view(np.uint32))
+
+
+def _holder():
+    import ctypes
+    import os
+    path = os.path.join(os.path.dirname(__file__), "native", "libspinner.so")
+    assert os.path.exists(path), "tests/native/libspinner.so is not built (run __graft_entry__.build())"
+    h = ctypes.CDLL(path)
+    h.spinner_start.argtypes = [ctypes.c_int, ctypes.c_double]
+    h.spinner_wait_resident.argtypes = [ctypes.c_double]
+    return h
+
+
+@pytest.mark.parametrize("held", [1, 32])
+def test_bitwise_while_foreign_kernel_holds_cus(held):
+    # the score kernel's blocks on held CUs start late; the resident ones take their work units
+    # from the ticket counter.  Results are bit-identical and the control block ends clean.
+    wl = W.make("causal_n1024", seed=3)
+    dev = _dev(wl)
+    ws = ix.alloc_workspace(wl.T, wl.Tkv, wl.B, wl.max_seqlen_k)
+    ref = _run(wl, dev, workspace=ws)
+    h = _holder()
+    for hold_us in (50.0, 400.0):
+        torch.cuda.synchronize()
+        assert h.spinner_start(held, hold_us) == 0
+        assert h.spinner_wait_resident(1000.0) == 0
+        got = _run(wl, dev, workspace=ws)
+        assert h.spinner_sync() == 0
+        assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1].view(np.uint32), got[1].view(np.uint32))
+        assert ix.read_status(ws) == (0, 0, 0)
