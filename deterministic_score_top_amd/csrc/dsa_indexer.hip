@@ -105,16 +105,8 @@ int launch_scores(const Call& c, hipStream_t stream) {
     // the knob counts 64-key tiles; units hold whole kernel tiles
     chunk = (int)(((int64_t)c.tuning->key_chunk_tiles * 64 + dsa::kTileKeys - 1) / dsa::kTileKeys);
   }
-  if (chunk == 0) {
-    // Units should be few (each start reloads the query block) but numerous enough to balance:
-    // about two per resident block, from an upper bound of the work in 64-key tiles.
-    const int64_t key_tiles = (L + dsa::kTileKeys - 1) / dsa::kTileKeys;
-    const int64_t work = (int64_t)max_tiles * key_tiles;
-    int64_t ct = work / (2 * (int64_t)grid_default);
-    if (ct < 1) ct = 1;
-    if (ct > key_tiles) ct = key_tiles;
-    chunk = (int)ct;
-  }
+  // chunk 0: the kernel picks the key chunk from the batch's total work (it alone reads the
+  // segment tables)
   if ((int64_t)chunk * dsa::kTileKeys > (int64_t)1 << 30) return DSA_ERR_SHAPE;
 
   dsa::ScoreParams p;

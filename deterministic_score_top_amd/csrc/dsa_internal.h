@@ -44,7 +44,7 @@ struct ScoreParams {
   int64_t ld;
   uint32_t* ctrl;
   int32_t B, T, Tkv, Lmax;
-  int32_t chunk_tiles;  // keys per unit = chunk_tiles * kTileKeys
+  int32_t chunk_tiles;  // keys per unit = chunk_tiles * kTileKeys; 0 = chosen by the kernel
   int32_t max_tiles;    // capacity of the LDS tile table
   int32_t store_keys;   // 1: store order-preserving 32-bit keys instead of FP32 scores
 };
