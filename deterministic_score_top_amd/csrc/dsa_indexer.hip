@@ -135,8 +135,11 @@ int check_common(const dsa_indexer_shape* shape, const void* q, const void* k, c
                  const void* workspace) {
   int rc = check_shape(shape);
   if (rc) return rc;
-  if (!q || !k || !w || !cu_q || !cu_k || !workspace) return DSA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(w) || !aligned16(workspace)) return DSA_ERR_ALIGN;
+  // q and w may be NULL when there are no queries, k when there are no keys
+  const bool has_q = shape->total_q > 0, has_k = shape->total_k > 0;
+  if ((has_q && (!q || !w)) || (has_k && !k) || !cu_q || !cu_k || !workspace) return DSA_ERR_NULL;
+  if ((q && !aligned16(q)) || (k && !aligned16(k)) || (w && !aligned16(w)) || !aligned16(workspace))
+    return DSA_ERR_ALIGN;
   if (!aligned4(cu_q) || !aligned4(cu_k) || (offs && !aligned4(offs))) return DSA_ERR_ALIGN;
   return DSA_OK;
 }
@@ -175,8 +178,8 @@ int dsa_indexer_topk_ex(const dsa_indexer_shape* shape, const void* q, const voi
   int rc = check_common(shape, q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets, workspace);
   if (rc) return rc;
   if (topk < 1 || topk > dsa::kMaxTopk) return DSA_ERR_SHAPE;
-  if (!out_ids || !out_scores) return DSA_ERR_NULL;
-  if (!aligned16(out_ids) || !aligned16(out_scores)) return DSA_ERR_ALIGN;
+  if (shape->total_q > 0 && (!out_ids || !out_scores)) return DSA_ERR_NULL;
+  if ((out_ids && !aligned16(out_ids)) || (out_scores && !aligned16(out_scores))) return DSA_ERR_ALIGN;
   if (workspace_bytes < dsa_indexer_workspace_size(shape)) return DSA_ERR_WORKSPACE;
   if (!device_info()) return DSA_ERR_DEVICE;
   if (profiler && profiler->used >= profiler->capacity) return DSA_ERR_SHAPE;

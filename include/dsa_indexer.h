@@ -32,6 +32,7 @@
  *   - All data pointers are caller-owned DEVICE memory on the current HIP device.  The
  *     library allocates nothing, frees nothing and never synchronises the stream.
  *   - Tensors are dense row-major; q, k, w, out_* and workspace must be 16-byte aligned.
+ *     q, w and out_* may be NULL when total_q is 0, and k when total_k is 0.
  *   - Host-side arguments are validated; device-resident tables (cu_seqlens, offsets) are
  *     validated by the kernel, which then skips the call's work and raises a status bit
  *     in the workspace (read with dsa_indexer_read_status) instead of touching memory out
@@ -63,7 +64,8 @@ extern "C" {
 /* Device status bits, left in the workspace control block by the kernels. */
 #define DSA_STATUS_CORRUPT_COUNTER 0x1u /* work-unit counter was not zero at entry          */
 #define DSA_STATUS_BAD_SEGMENTS 0x2u    /* cu_seqlens not 0-based, non-decreasing, ending at T/Tkv */
-#define DSA_STATUS_SEQLEN_BOUND 0x4u    /* a segment has more keys than max_seqlen_k         */
+#define DSA_STATUS_SEQLEN_BOUND 0x4u    /* a segment has more keys than max_seqlen_k; its
+                                           queries see only its first max_seqlen_k keys  */
 
 /* Supported sizes. */
 #define DSA_NUM_HEADS 64
@@ -83,8 +85,9 @@ typedef struct dsa_indexer_shape {
 
 /*
  * Bytes of workspace the top-k call needs for `shape`: a 256-byte control block (work-unit
- * counter, exit counter, status word) followed by the FP32 score rows, T rows of
- * round_up(max_seqlen_k, 64) floats.  Returns 0 if the shape is invalid.
+ * counter, exit counter, status word) followed by the score rows, T rows of
+ * round_up(max_seqlen_k, 64) 32-bit words (order-preserving keys of the FP32 scores).
+ * Returns 0 if the shape is invalid.
  */
 size_t dsa_indexer_workspace_size(const dsa_indexer_shape* shape);
 

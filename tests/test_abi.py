@@ -84,6 +84,21 @@ def test_argument_errors():
     assert _call(bad, GOOD) == -3
 
 
+def test_empty_inputs_may_be_null():
+    # no queries: q, w and the outputs may be NULL; no keys: k may be NULL.  With the arguments
+    # accepted, the call reaches the device check (-6 on a host without the GPU, 0 on the GPU
+    # for T = 0, which enqueues nothing).
+    no_q = ix.make_shape(0, 64, 1, 64)
+    r = _call(no_q, (None, 0x20000, None, 0x40000, 0x50000, None, None, None, 0x80000))
+    assert r in (0, -6)
+    no_k = ix.make_shape(16, 0, 1, 64)
+    r = _call(no_k, (0x10000, None, 0x30000, 0x40000, 0x50000, None, 0x60000, 0x70000, 0x80000))
+    assert r in (0, -6)
+    s = ix.make_shape(16, 64, 1, 64)
+    assert _call(s, _with(1, None)) == -1          # k NULL with keys present
+    assert _call(s, _with(6, None)) == -1          # out_ids NULL with queries present
+
+
 def test_scores_argument_errors():
     L = ix.lib()
     s = ix.make_shape(16, 64, 1, 64)

@@ -305,3 +305,39 @@ def test_bitwise_while_foreign_kernel_holds_cus(held):
         assert h.spinner_sync() == 0
         assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1].view(np.uint32), got[1].view(np.uint32))
         assert ix.read_status(ws) == (0, 0, 0)
+
+
+def test_seqlen_bound_flagged_and_truncated():
+    # a segment with more keys than max_seqlen_k: the status bit is raised and its queries see
+    # only the segment's first max_seqlen_k keys
+    wl = W.random_segments([30], [300], [280], topk=64, seed=50)
+    q, k, w, cq, ck, offs = _dev(wl)
+    ws = ix.alloc_workspace(wl.T, wl.Tkv, wl.B, 200)
+    ids, sc = ix.topk(q, k, w, cq, ck, offs, topk=64, workspace=ws, max_seqlen_k=200)
+    torch.cuda.synchronize()
+    st, tk, dn = ix.read_status(ws)
+    assert st & ix.STATUS_SEQLEN_BOUND and tk == 0 and dn == 0
+    cut = W.Workload("cut", wl.q, wl.k[:200].contiguous(), wl.w, wl.cu_seqlens_q,
+                     torch.tensor([0, 200], dtype=torch.int32), wl.q_pos_offsets, 64, 200)
+    oi, osc, det = _oracle(cut)
+    check_rows(ids.cpu().numpy(), sc.cpu().numpy(), range(cut.T), oi, osc, det, 64)
+
+
+def test_no_queries_and_no_keys():
+    d = "cuda"
+    # no queries: nothing is enqueued and empty outputs come back
+    q = torch.empty((0, 64, 128), dtype=torch.bfloat16, device=d)
+    w = torch.empty((0, 64), dtype=torch.float32, device=d)
+    k = torch.randn((50, 128), device=d).to(torch.bfloat16)
+    cq = torch.tensor([0, 0], dtype=torch.int32, device=d)
+    ck = torch.tensor([0, 50], dtype=torch.int32, device=d)
+    ids, sc = ix.topk(q, k, w, cq, ck, None, topk=8, max_seqlen_k=50)
+    torch.cuda.synchronize()
+    assert ids.shape == (0, 8) and sc.shape == (0, 8)
+    # no keys at all: every row is padding
+    wl = W.random_segments([5, 7], [0, 0], [3, 0], topk=4, seed=51)
+    dq, dk, dw, dcq, dck, doffs = _dev(wl)
+    assert dk.shape[0] == 0
+    ids, sc = ix.topk(dq, dk, dw, dcq, dck, doffs, topk=4, max_seqlen_k=1)
+    torch.cuda.synchronize()
+    assert bool((ids == -1).all()) and bool(torch.isneginf(sc).all())
