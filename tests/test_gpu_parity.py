@@ -341,3 +341,35 @@ def test_no_queries_and_no_keys():
     ids, sc = ix.topk(dq, dk, dw, dcq, dck, doffs, topk=4, max_seqlen_k=1)
     torch.cuda.synchronize()
     assert bool((ids == -1).all()) and bool(torch.isneginf(sc).all())
+
+
+def test_graph_capture_replays_match_eager():
+    # the call enqueues only its kernels (no allocation, memset or host sync), so it can be
+    # captured; replays interleaved with eager work and synchronisation must each match the
+    # eager result bit for bit (the work-unit counter resets itself at the end of every run)
+    wl = W.random_segments([100, 37], [900, 300], [800, 100], topk=128, seed=60)
+    q, k, w, cq, ck, offs = _dev(wl)
+    ws = ix.alloc_workspace(wl.T, wl.Tkv, wl.B, wl.max_seqlen_k)
+    oi = torch.empty((wl.T, 128), dtype=torch.int32, device="cuda")
+    osc = torch.empty((wl.T, 128), dtype=torch.float32, device="cuda")
+    kw = dict(topk=128, workspace=ws, max_seqlen_k=wl.max_seqlen_k, out_ids=oi, out_scores=osc)
+    ix.topk(q, k, w, cq, ck, offs, **kw)
+    torch.cuda.synchronize()
+    ref = (oi.cpu().numpy().copy(), osc.cpu().numpy().copy())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            ix.topk(q, k, w, cq, ck, offs, **kw)
+    torch.cuda.current_stream().wait_stream(side)
+    for r in range(4):
+        oi.fill_(7)
+        osc.fill_(7.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(oi.cpu().numpy(), ref[0]), r
+        assert np.array_equal(osc.cpu().numpy().view(np.uint32), ref[1].view(np.uint32)), r
+        ix.topk(q, k, w, cq, ck, offs, **kw)       # eager work between replays
+        torch.cuda.synchronize()
+        assert ix.read_status(ws) == (0, 0, 0)
