@@ -286,8 +286,10 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
     // decode u -> (tile g, chunk c) -> (segment b, tile i)
     // (every lane computes the same values; readfirstlane makes that visible to the compiler so
     // the unit's scalars and buffer resources stay in scalar registers)
-    const int g = __builtin_amdgcn_readfirstlane(upper_bound_u32(unit_pf, ntiles + 1, u) - 1);
-    const int c = __builtin_amdgcn_readfirstlane((int)(u - unit_pf[g]));
+    // (one unit per tile, the usual case, needs no search)
+    const bool whole = units == (uint32_t)ntiles;
+    const int g = whole ? (int)u : __builtin_amdgcn_readfirstlane(upper_bound_u32(unit_pf, ntiles + 1, u) - 1);
+    const int c = whole ? 0 : __builtin_amdgcn_readfirstlane((int)(u - unit_pf[g]));
     const int j = __builtin_amdgcn_readfirstlane(upper_bound_u32(seg_tp, B + 1, (uint32_t)g) - 1);
     const int b = __builtin_amdgcn_readfirstlane((int)seg_ord[j]);
     const int ntile_b = __builtin_amdgcn_readfirstlane((int)(seg_tp[j + 1] - seg_tp[j]));
