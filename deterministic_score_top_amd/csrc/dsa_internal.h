@@ -28,6 +28,7 @@ constexpr int kRowAlign = 64;                            // score rows padded to
 constexpr int kCtrlTicket = 0;
 constexpr int kCtrlDone = 1;
 constexpr int kCtrlStatus = 2;
+constexpr int kCtrlExpected = 3;  // final counter value of the score kernel, for the select kernel's check
 
 constexpr uint32_t kStatusCorruptCounter = 0x1u;
 constexpr uint32_t kStatusBadSegments = 0x2u;
@@ -57,7 +58,7 @@ struct SelectParams {
   const int32_t* offs;
   int32_t* out_ids;
   float* out_scores;
-  const uint32_t* ctrl;
+  uint32_t* ctrl;  // block 0 checks and resets the work-unit counter left by the score kernel
   int32_t B, T, Tkv, Lmax, topk;
 };
 

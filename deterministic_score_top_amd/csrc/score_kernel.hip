@@ -145,7 +145,11 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
   const int B = p.B;
 
   // ---- per-block plan: validate segments, tiles per segment, units per tile -------------
-  if (tid == 0) slot[2] = 0;
+  // (the block's first ticket is drawn now; its latency overlaps the plan)
+  if (tid == 0) {
+    slot[2] = 0;
+    slot[0] = (int)atomicAdd(p.ctrl + kCtrlTicket, 1u);
+  }
   __syncthreads();
   {
     int flags = 0;
@@ -267,10 +271,11 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
   }
 
   // ---- ticket loop ------------------------------------------------------------------------
-  if (tid == 0) slot[0] = (int)atomicAdd(p.ctrl + kCtrlTicket, 1u);
-  __syncthreads();
   uint32_t u = (uint32_t)slot[0];
   if (tid == 0 && u >= units + gridDim.x) atomicOr(p.ctrl + kCtrlStatus, kStatusCorruptCounter);
+  // With a select kernel to follow, the counter is checked and reset there (stream order puts
+  // it after every block of this kernel): record the value it must reach.
+  if (p.store_keys && blockIdx.x == 0 && tid == 0) p.ctrl[kCtrlExpected] = units + gridDim.x;
 
   // lane roles (fixed for the whole kernel): one query per wave; A row / B column n, lane half hf
   const int n = lane & 31;
@@ -479,8 +484,9 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
     ++iter;
   }
 
-  // ---- exit: the last block out resets the counters ----------------------------------------
-  if (tid == 0) {
+  // ---- exit: without a select kernel to follow, the last block out checks and resets the
+  // counters --------------------------------------------------------------------------------
+  if (!p.store_keys && tid == 0) {
     __threadfence();
     const uint32_t prev = atomicAdd(p.ctrl + kCtrlDone, 1u);
     if (prev == gridDim.x - 1) {

@@ -248,6 +248,13 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int topk = p.topk;
   const bool bad = (p.ctrl[kCtrlStatus] & kStatusBadSegments) != 0;
+  if (blockIdx.x == 0 && tid == 0) {
+    // the score kernel drew units + grid tickets; anything else means the counter was not zero
+    // when it started.  Reset for the next call (this kernel runs after the score kernel).
+    if (p.ctrl[kCtrlTicket] != p.ctrl[kCtrlExpected]) atomicOr(p.ctrl + kCtrlStatus, kStatusCorruptCounter);
+    p.ctrl[kCtrlTicket] = 0u;
+    p.ctrl[kCtrlDone] = 0u;
+  }
   const bool cached = p.B <= kSegCache;
   if (cached) {
     for (int i = tid; i <= p.B; i += NT) {
