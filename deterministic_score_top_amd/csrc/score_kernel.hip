@@ -1,23 +1,28 @@
 // Score phase of the DSA indexer top-k scan on gfx950 (CDNA4).
 //
 // Computes I[t, s] = sum_h w[t, h] * max(0, q[t, h, :] . k[s, :]) for every causally visible
-// (query, key) pair of every segment and writes it to a dense FP32 row per query
-// (out[t * ld + j], j = segment-local key index).  Score definition: the lightning-indexer
-// form the scan of flashinfer PR #8691 (description; vendoring note) is built on.
+// (query, key) pair of every segment and writes it to a dense row per query (out[t * ld + j],
+// j = segment-local key index): the FP32 score, or for the top-k call its order-preserving
+// 32-bit key.  Score definition: the lightning-indexer form the scan of flashinfer PR #8691
+// (description; vendoring note) is built on.
 //
 // Work decomposition.  A work unit is (segment, tile of 8 consecutive queries, chunk of
 // keys).  The grid is persistent: every block draws unit numbers from a counter in the
 // workspace (the ticket word of the same page's description: blocks that are resident take
 // the next unit, so a foreign kernel holding some CUs does not push units into a second
-// wave).  Units are numbered segment by segment, and inside a segment from the last query
-// tile (most visible keys) to the first, so the cheapest units run last.  The last block to
-// leave resets the counter, so steady-state calls pay no reset.
+// wave).  Every block derives the same plan from the segment tables: segments longest tile
+// first, inside a segment from the last query tile (most visible keys) to the first, so the
+// cheapest units run last; whole tiles per unit unless the batch's longest tiles are long
+// next to a block's share, then even pieces of at most a quarter of that share.  The counter
+// is checked and reset by the select kernel that follows (or, for the scores-only call, by
+// the last block to leave), so steady-state calls pay no reset.
 //
 // Inside a unit (512 threads = 8 waves, one query per wave):
 //   * each wave holds the BF16 A operand of its query (64 heads x 128 dims: 2 row blocks of
 //     32 rows x 8 K-steps of 16) in VGPRs, loaded once per unit, and the query's head weights;
-//   * 64-key tiles of k are staged in LDS (double buffered, 16-byte chunks XOR-swizzled by
-//     key so the B-operand reads and the tile writes are bank-conflict free);
+//   * 64-key tiles of k land in LDS two tiles ahead (three buffers) by buffer loads that
+//     write LDS directly, 16-byte chunks XOR-swizzled by key so the B-operand reads are
+//     bank-conflict free;
 //   * per tile: 2 column blocks of 32 keys x 2 row blocks x 8 K-steps of
 //     v_mfma_f32_32x32x16_bf16 (FP32 accumulate, d ascending);
 //   * epilogue in registers: lane half hf holds heads 32*rb + 16*hf + i (i = 0..15) of key
