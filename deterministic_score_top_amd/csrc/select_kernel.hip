@@ -34,7 +34,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kHistBits = 10;
 constexpr int kHistBins = 1 << kHistBits;
-constexpr int kCandCap = 3072;    // survivors per row held in LDS
+constexpr int kCandCap = 3072;    // survivors per row held in LDS (256-thread rows)
+constexpr int kCandCapWide = 4096;  // the same for 1024-thread rows (16 waves, 256 each)
 constexpr int kSegCache = 256;    // segments whose tables are cached in LDS
 constexpr int kSampleStride = 4;  // sample = every key of every 4th step
 constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor word 3: raw 32-bit data, range-checked
@@ -60,7 +61,7 @@ __device__ __forceinline__ void wave_prefix3(uint32_t cnt, uint32_t& excl, uint3
 template <int NT>
 struct alignas(16) Smem {
   static constexpr int NW = NT / 64;
-  static constexpr int R = kCandCap / NW;  // survivors per wave region
+  static constexpr int R = (NT >= 1024 ? kCandCapWide : kCandCap) / NW;  // survivors per wave region
   static_assert(R % 256 == 0, "wave regions are read in steps of 256 entries");
   uint32_t hist[kHistBins];
   uint32_t ckey[NW][R];
@@ -579,6 +580,13 @@ hipError_t launch_variant(const SelectParams& p, hipStream_t s) {
 
 hipError_t launch_select(const SelectParams& p, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipErrorInvalidDevice;
+  // Few rows (a split tail, a handful of decode queries) leave most CUs idle: give each row
+  // 16 waves instead of 4, so its passes over the keys take a quarter of the steps.
+  if (4 * p.T <= cus) return launch_variant<1024>(p, s);
   return launch_variant<256>(p, s);
 }
 
