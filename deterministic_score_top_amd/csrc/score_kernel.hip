@@ -438,20 +438,25 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
     auto outbits = [&](float v) -> uint32_t { return keys_out ? score_key(v) : __float_as_uint(v); };
     constexpr int kPhases = kTileKeys / 32;
     static_assert(kPhases % 2 == 0, "column blocks alternate between two accumulator pairs");
+    constexpr int kStores = kPhases / 2;  // score stores per tile
+    static_assert(kStores + kStageChunks < 16, "vector-memory wait counts fit the 4-bit field");
     f32x16 c0a, c0b, c1a = f32x16{}, c1b = f32x16{};
     auto tile = [&](const unsigned char* buf, float (&sc)[kPhases]) {
 #pragma unroll
       for (int cb = 0; cb < kPhases; ++cb)
         sc[cb] = (cb & 1) ? phase(buf, cb, c1a, c1b, c0a, c0b) : phase(buf, cb, c0a, c0b, c1a, c1b);
     };
+    // Both lane halves hold every column-block sum, so one store covers two blocks: lane half
+    // 0 writes block 2i, lane half 1 block 2i+1 (kStores = kPhases / 2 stores per tile).
     auto store_tile = [&](const float (&sc)[kPhases], int kt_prev, int kt0) {
-      __builtin_amdgcn_raw_buffer_store_b32(
-          outbits(sc[0]), ors, (hf == 0 && kt_prev >= 0) ? (kt_prev + 32 * (kPhases - 1) + n) * 4 : kDropOffset,
-          0, 0);
+      auto offset = [&](int cb) -> int {
+        if (cb == 0) return kt_prev >= 0 ? (kt_prev + 32 * (kPhases - 1) + n) * 4 : kDropOffset;
+        return (kt0 + 32 * (cb - 1) + n) * 4;
+      };
 #pragma unroll
-      for (int cb = 1; cb < kPhases; ++cb)
-        __builtin_amdgcn_raw_buffer_store_b32(outbits(sc[cb]), ors,
-                                              hf == 0 ? (kt0 + 32 * (cb - 1) + n) * 4 : kDropOffset, 0, 0);
+      for (int i = 0; i < kPhases / 2; ++i)
+        __builtin_amdgcn_raw_buffer_store_b32(outbits(hf ? sc[2 * i + 1] : sc[2 * i]), ors,
+                                              hf ? offset(2 * i + 1) : offset(2 * i), 0, 0);
     };
 
     const int ntl = kend > kbeg ? ceil_div(kend - kbeg, kTileKeys) : 0;
@@ -468,16 +473,16 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
     // barrier after it), tile t is multiplied, then this wave waits until its part of tile t+1
     // is in LDS, and the barrier makes all of tile t+1 visible.  Vector memory operations
     // complete in issue order; after tile t+1's loads this wave has issued tile t-1's score
-    // stores (kPhases) and, when present, tile t+2's loads (kStageChunks), so waiting until at
+    // stores (kStores) and, when present, tile t+2's loads (kStageChunks), so waiting until at
     // most that many are outstanding covers tile t+1.
     auto step = [&](unsigned char* cur, unsigned char* next2, int t) {
       const int kt0 = kbeg + t * kTileKeys;
       if (t + 2 < ntl) ldsload(next2, kt0 + 2 * kTileKeys);
       tile(cur, sc);
       if (t + 2 < ntl) {
-        __builtin_amdgcn_s_waitcnt(kWaitVm | (kPhases + kStageChunks));
+        __builtin_amdgcn_s_waitcnt(kWaitVm | (kStores + kStageChunks));
       } else {
-        __builtin_amdgcn_s_waitcnt(kWaitVm | kPhases);
+        __builtin_amdgcn_s_waitcnt(kWaitVm | kStores);
       }
       // A plain barrier: a fenced one would also wait for tile t+2's loads.  The memory
       // clobber keeps the compiler from moving LDS accesses across it; this wave's reads of
