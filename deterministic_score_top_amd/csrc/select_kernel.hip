@@ -312,8 +312,16 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
 
     // ---- A: threshold from a sample: every key of every 4th step of each wave's span --------
     for (int i = tid; i < kHistBins; i += NT) sm.hist[i] = 0u;  // free since the last row's barriers
+    // The wave's sample also goes to its (still unused) survivor region when it fits, so the
+    // histogram pass below reads it from LDS instead of from the row again.
+    const int sample_steps = ((ks.span >> 8) + kSampleStride - 1) / kSampleStride;
+    const bool staged = sample_steps * 256 <= R;
     uint32_t smin = 0xffffffffu, smax = 0u, scnt = 0;
-    ks.each([&](int, const uint32_t (&k4)[4]) {
+    ks.each([&](int pos, const uint32_t (&k4)[4]) {
+      if (staged) {
+        const int idx = ((pos - ks.base) >> 8) / kSampleStride;  // sampled step of this lane's keys
+        *reinterpret_cast<u32x4*>(&sm.ckey[wv][idx * 256 + 4 * lane]) = u32x4{k4[0], k4[1], k4[2], k4[3]};
+      }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         smin = min(smin, k4[c] - 1u);  // invalid (0) wraps to the top and drops out
@@ -346,11 +354,20 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
       const uint32_t srange = smax - smin;
       const int sbits = 32 - __clz((int)srange);
       const int sshift = max(sbits - kHistBits, 0);
-      ks.each([&](int, const uint32_t (&k4)[4]) {
+      auto bin_sample = [&](const uint32_t (&k4)[4]) {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
           if (k4[c]) atomicAdd(&sm.hist[(k4[c] - smin) >> sshift], 1u);
-      }, kSampleStride);
+      };
+      if (staged) {
+        for (int idx = 0; idx < sample_steps; ++idx) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.ckey[wv][idx * 256 + 4 * lane]);
+          const uint32_t k4[4] = {v[0], v[1], v[2], v[3]};
+          bin_sample(k4);
+        }
+      } else {
+        ks.each([&](int, const uint32_t (&k4)[4]) { bin_sample(k4); }, kSampleStride);
+      }
       __syncthreads();
       find_bin<NT>(sm, kHistBins, r);  // ends with a barrier: the histogram is free afterwards
       theta = smin + (sm.bcast[0] << sshift);
