@@ -6,23 +6,29 @@
 // partitioning) is the total order (key descending, position descending) on the row, and the
 // selected keys are written with ids ascending.
 //
-// Per row (one workgroup; workgroups loop over rows):
+// Per row (one workgroup of 256 threads, or 1024 when the batch has few rows; workgroups loop
+// over rows):
 //   A  a sample of the row (1/4 of it) gives a threshold theta = lower edge of the sample
-//      histogram bin that holds a rank a few standard deviations past k*m/n, so that, with
-//      overwhelming probability, theta is below the k-th key while only ~1.3k keys are >= theta;
+//      histogram bin that holds a rank four standard deviations past k*m/n, so that, with
+//      overwhelming probability, theta is below the k-th key while only a few hundred keys
+//      more than k are >= theta (the sample is kept in LDS for its histogram when it fits);
 //   B  one pass compares every key with theta and copies the survivors (key, position) into
 //      per-wave LDS regions in position order (ballots + mbcnt, no atomics);
 //   C  the exact k-th key T is found over the survivors with range-normalised LDS histograms
-//      (digits of up to 10 bits), together with how many keys equal T and how many of those are left
-//      out (the lowest positions);
+//      (digits of up to 10 bits; once the bin holding rank k has at most 64 keys, one wave
+//      ranks them directly), together with how many keys equal T and how many of those are
+//      left out (the lowest positions);
 //   D  the survivors are written in position order: wave w starts at the fixed-order sum of
 //      the selected counts of waves 0..w-1, lanes are ranked with ballots and mbcnt.
 // If the sample's guess fails (fewer than k survivors, or a region overflows), an exact
 // fallback resolves T with histograms over every key and writes from the whole row.  Results
 // never depend on which path ran.
 //
-// Passes read the row from the workspace rows written by the score phase; after the first read
-// they are L2/MALL-resident.  A row costs about 1.25 reads when the sample's guess holds.
+// Passes read the row from the workspace rows written by the score phase (L2/MALL-resident
+// for rows of moderate length).  A row costs about 1.25 reads when the sample's guess holds.
+// Wave reductions and scans use DPP lane moves; row loads are range-checked buffer loads
+// issued several steps at a time.  The first workgroup also checks and resets the work-unit
+// counter the score kernel left in the control block.
 
 #include "dsa_internal.h"
 #include "wave_ops.h"
