@@ -177,6 +177,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
   uint32_t units = 0;
   int ntiles = 0;
   int chunk_keys = kTileKeys;
+  bool whole_tiles = false;
   if (!(plan_flags & 1)) {
     // Segment order: longest tile first (the key is the first tile's key-tile count), ties by
     // segment index, so that the longest work units of the whole batch start first.  Every
@@ -282,8 +283,17 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
       }
     }
     chunk_keys = chunk_tiles * kTileKeys;
-    for (int g = tid; g < ntiles; g += kScoreThreads) unit_pf[g] = (unit_pf[g] + chunk_tiles - 1) / chunk_tiles;
+    if (tid == 0) slot[8] = 0;
     __syncthreads();
+    bool one_each = true;  // every tile is exactly one unit (keyless tiles have none)
+    for (int g = tid; g < ntiles; g += kScoreThreads) {
+      const uint32_t nu = (unit_pf[g] + chunk_tiles - 1) / chunk_tiles;
+      unit_pf[g] = nu;
+      one_each &= nu == 1u;
+    }
+    if (!one_each) atomicOr(&slot[8], 1);
+    __syncthreads();
+    whole_tiles = slot[8] == 0;
     block_scan_excl(unit_pf, ntiles, part);
     units = unit_pf[ntiles];
   }
@@ -316,7 +326,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
     // (every lane computes the same values; readfirstlane makes that visible to the compiler so
     // the unit's scalars and buffer resources stay in scalar registers)
     // (one unit per tile, the usual case, needs no search)
-    const bool whole = units == (uint32_t)ntiles;
+    const bool whole = whole_tiles;
     const int g = whole ? (int)u : __builtin_amdgcn_readfirstlane(upper_bound_u32(unit_pf, ntiles + 1, u) - 1);
     const int c = whole ? 0 : __builtin_amdgcn_readfirstlane((int)(u - unit_pf[g]));
     const int j = __builtin_amdgcn_readfirstlane(upper_bound_u32(seg_tp, B + 1, (uint32_t)g) - 1);

@@ -373,3 +373,20 @@ def test_graph_capture_replays_match_eager():
         ix.topk(q, k, w, cq, ck, offs, **kw)       # eager work between replays
         torch.cuda.synchronize()
         assert ix.read_status(ws) == (0, 0, 0)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_batches(seed):
+    # seeded random segment tables: lengths from empty to a few thousand keys, offsets that put
+    # queries before, inside and past their segment's keys, k from 1 to 2048; exercises the
+    # plan's segment order and chunk choice and both select widths against the oracle.  (Seed
+    # 1008 has as many units as tiles while one tile is split in five and four keyless tiles
+    # have none: a unit-to-tile shortcut keyed on the totals alone skipped key columns there.)
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.integers(1, 9))
+    ql = rng.integers(0, 40, B).tolist()
+    kl = [int(x) for x in rng.choice([0, 5, 64, 300, 1000, 2500], B)]
+    offs = [int(rng.integers(-20, k + 40)) for k in kl]
+    topk = int(rng.choice([1, 7, 64, 256, 1000, 2048]))
+    wl = W.random_segments(ql, kl, offs, topk=topk, seed=1000 + seed)
+    _check_all(wl)
