@@ -390,3 +390,25 @@ def test_random_batches(seed):
     topk = int(rng.choice([1, 7, 64, 256, 1000, 2048]))
     wl = W.random_segments(ql, kl, offs, topk=topk, seed=1000 + seed)
     _check_all(wl)
+
+
+def _random_table(rng, max_b=40, max_q=60):
+    B = int(rng.integers(1, max_b + 1))
+    ql = rng.integers(0, max_q, B).tolist()
+    kl = [int(x) for x in rng.choice([0, 1, 31, 64, 65, 200, 777, 2100], B)]
+    offs = [int(rng.integers(-30, k + 50)) for k in kl]
+    topk = int(rng.choice([1, 3, 16, 100, 512, 2048]))
+    return ql, kl, offs, topk
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_integer_batches_exact(seed):
+    # exact-arithmetic inputs over random tables, with random key-chunk and grid settings:
+    # scores bit-equal to the oracle's and id sets identical (ties resolved by the larger id),
+    # few distinct key vectors in half the cases so that long tie runs occur
+    rng = np.random.default_rng(2000 + seed)
+    ql, kl, offs, topk = _random_table(rng)
+    distinct = int(rng.choice([2, 5, 0])) or None
+    wl = W.integer_valued(ql, kl, offs, topk=topk, seed=2000 + seed, distinct_keys=distinct)
+    tuning = dict(key_chunk_tiles=int(rng.choice([0, 1, 2, 5])), grid_blocks=int(rng.choice([0, 1, 3, 37])))
+    _check_all(wl, exact=True, tuning=tuning)
