@@ -199,6 +199,19 @@ def random_segments(T_lens, K_lens, offsets, topk, H=H_DEFAULT, D=D_DEFAULT, see
     return Workload("random", q, k, w, cq, ck, o, topk, int(max(K_lens) if len(K_lens) else 0))
 
 
+def draw_grad(T: int, ld: int, seed: int = 0, integer: bool = False) -> torch.Tensor:
+    """Upstream gradients of the scores, FP32 [T, ld] in the scores-export row layout.
+
+    Gaussian N(0,1), or with integer=True dyadic values n/16, n in [-7, 7] (three
+    significant bits, exact in BF16 and in every FP32 product with the other
+    integer-valued inputs).
+    """
+    g = _gen(seed + 7919)
+    if integer:
+        return torch.randint(-7, 8, (T, ld), generator=g).to(torch.float32) / 16.0
+    return torch.randn((T, ld), generator=g, dtype=torch.float32)
+
+
 CONFIGS = {
     # name: (builder, description)
     "causal_n1024": lambda seed=0: single_causal(1024, 256, seed, "causal_n1024"),

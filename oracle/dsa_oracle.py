@@ -36,6 +36,20 @@ whole segment; one causal offset per segment (absent = 0); ids are global
 row indices of k; each row lists its ids in ascending order; padding slots
 hold id -1 and score -inf; -0 and +0 are the same score.
 
+Backward of the scores (same package page, the vendoring commit message: the
+deterministic package holds lightning-indexer logits kernels and their
+backward, with no floating-point atomics and the key-side gradient reduced
+from FP32 partials in a fixed tree).  The pages print no formula; the oracle
+takes the plain chain rule of the score above.  Given g[t, j] = dL/dI[t, s]
+for the visible keys s = first_t + j of query t (the layout of the scores
+export: row t, column j):
+        dw[t, h]    = sum_j g[t, j] * max(0, S[t, h, j])
+        dq[t, h, :] = sum_j g[t, j] * w[t, h] * [S[t, h, j] > 0] * k[s, :]
+        dk[s, :]    = sum_{t sees s} sum_h g[t, j] * w[t, h] * [S[t, h, j] > 0] * q[t, h, :]
+with S[t, h, j] = q[t, h, :] . k[s, :].  The ReLU's derivative at exactly 0
+is taken as 0 (the usual convention; the pages are silent).  Keys no query
+sees get dk = 0, queries that see no key get dq = dw = 0.
+
 Everything here is FP64: BF16 and FP32 inputs convert to FP64 exactly, the
 dot products use a library matmul, the head reduction a library
 matrix-vector product, and the selection a library lexicographic sort on
@@ -132,3 +146,41 @@ def topk_workload(wl, rows=None):
     cu_k = wl.cu_seqlens_k.numpy()
     offs = None if wl.q_pos_offsets is None else wl.q_pos_offsets.numpy()
     return topk_rows(q64, k64, w64, cu_q, cu_k, offs, wl.topk, rows)
+
+
+def row_backward(q64, k64, w64, t: int, first: int, n: int, g: np.ndarray):
+    """Query t's gradient terms for upstream gradients g[0..n-1] of its n visible scores.
+
+    Returns (dq[t] [H, D], dw[t] [H], its contribution to dk[first .. first+n-1] [n, D]).
+    """
+    H, D = q64.shape[1], q64.shape[2]
+    if n == 0:
+        return np.zeros((H, D)), np.zeros(H), np.zeros((0, D))
+    K = k64[first:first + n]                      # [n, D]
+    S = q64[t] @ K.T                              # [H, n] per-head dot products
+    on = S > 0.0                                  # ReLU derivative: 1 above zero, 0 at and below
+    dw = np.maximum(S, 0.0) @ g                   # [H]
+    G = np.where(on, w64[t][:, None] * g[None, :], 0.0)   # dL/dS [H, n]
+    return G @ K, dw, G.T @ q64[t]
+
+
+def backward_rows(q64, k64, w64, cu_q, cu_k, offs, grad):
+    """dq [T, H, D], dk [Tkv, D], dw [T, H] in FP64 for upstream gradients grad[t, j] (j < n_t read)."""
+    T, H, D = q64.shape
+    dq = np.zeros((T, H, D))
+    dw = np.zeros((T, H))
+    dk = np.zeros((k64.shape[0], D))
+    for t in range(T):
+        first, n = visible(cu_q, cu_k, offs, t)
+        g = np.asarray(grad[t, :n], dtype=np.float64)
+        dq[t], dw[t], part = row_backward(q64, k64, w64, t, first, n, g)
+        dk[first:first + n] += part
+    return dq, dk, dw
+
+
+def backward_workload(wl, grad):
+    """Oracle backward on a generated workload; grad is a CPU FP32 tensor or array [T, >= n_t]."""
+    q64, k64, w64 = from_torch(wl.q, wl.k, wl.w)
+    g = grad.double().numpy() if hasattr(grad, "double") else np.asarray(grad, dtype=np.float64)
+    offs = None if wl.q_pos_offsets is None else wl.q_pos_offsets.numpy()
+    return backward_rows(q64, k64, w64, wl.cu_seqlens_q.numpy(), wl.cu_seqlens_k.numpy(), offs, g)

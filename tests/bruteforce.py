@@ -48,3 +48,38 @@ def brute_topk(q, k, w, cu_q, cu_k, offs, topk, H, D):
         scores = [v for v, _ in kept] + [None] * (topk - len(kept))
         out.append((ids, scores))
     return out
+
+
+def visible_count(cu_q, cu_k, offs, t):
+    """(segment, first key id, visible key count) of query t, by a linear scan."""
+    for b in range(len(cu_q) - 1):
+        if cu_q[b] <= t < cu_q[b + 1]:
+            pos = (0 if offs is None else offs[b]) + t - cu_q[b]
+            nk = cu_k[b + 1] - cu_k[b]
+            return b, cu_k[b], max(0, min(pos + 1, nk))
+    raise ValueError(t)
+
+
+def exact_dots(q, k, cu_q, cu_k, offs, H, D):
+    """Every visible per-head dot product, exactly: {(t, h, s): Fraction}."""
+    out = {}
+    for t in range(len(q)):
+        _, first, n = visible_count(cu_q, cu_k, offs, t)
+        for s in range(first, first + n):
+            for h in range(H):
+                acc = Fraction(0)
+                for d in range(D):
+                    acc += q[t][h * D + d] * k[s][d]
+                out[(t, h, s)] = acc
+    return out
+
+
+def exact_loss(q, k, w, g, cu_q, cu_k, offs, H, D):
+    """L = sum_t sum_j g[t][j] * I[t, first_t + j] over the visible keys, exactly."""
+    dots = exact_dots(q, k, cu_q, cu_k, offs, H, D)
+    total = Fraction(0)
+    for (t, h, s), v in dots.items():
+        if v > 0:
+            _, first, _ = visible_count(cu_q, cu_k, offs, t)
+            total += g[t][s - first] * w[t][h] * v
+    return total
