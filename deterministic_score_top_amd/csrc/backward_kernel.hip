@@ -1,0 +1,556 @@
+// Backward of the indexer scores on gfx950 (CDNA4): dq, dk and dw from the upstream gradient
+// g[t, j] = dL/dI[t, s] of every visible (query t, key s = first_t + j) pair.
+//
+// With S[t, h, s] = q[t, h, :] . k[s, :] and the score I[t, s] = sum_h w[t, h] * max(0, S):
+//     dw[t, h]    = sum_s g * max(0, S)
+//     dq[t, h, :] = w[t, h] * sum_s g * [S > 0] * k[s, :]
+//     dk[s, :]    = sum_t sum_h w[t, h] * g * [S > 0] * q[t, h, :]
+// (flashinfer PR #8691, the vendoring commit message: the deterministic package carries the
+// lightning-indexer logits kernels and their backward, with no floating-point atomics and
+// the key-side gradient reduced from FP32 partials in a fixed tree.)  The derivative of the
+// ReLU at exactly 0 is 0.
+//
+// Three kernels, no atomics on any gradient, every sum in a fixed order:
+//   * dq/dw kernel, query-major: a unit is 4 consecutive queries of one segment; wave w takes
+//     query w/2 and heads 32*(w%2) .. +31.  Per 64-key tile it recomputes S^T = K . Q^T
+//     (v_mfma_f32_32x32x16_bf16, K tile from LDS, Q in VGPRs), forms dw partials in FP32 and
+//     the BF16 operand G' = g * [S > 0] (w is factored out of the key sum and applied once at
+//     the end), and accumulates dq += G' . K with the K operand read key-major from the same
+//     LDS tile by ds_read_b64_tr_b16.
+//   * dk kernel, key-major: a unit is (one 64-key tile, one of 4 parts of the queries that see
+//     it).  Wave w takes keys 32*(w%2) .. +31 of the tile and query stream w/2; the 4 streams
+//     take the part's queries in turn.  Per query: S = Q . K^T (K in VGPRs for the whole
+//     unit, Q from LDS), the BF16 operand G'' = w * g * [S > 0], and dk^T += Q^T . G'' with
+//     the Q^T operand read head-major from LDS by ds_read_b64_tr_b16.  The 4 streams' FP32
+//     sums are added in a fixed tree ((0 + 1) + (2 + 3)) and stored as the unit's partial.
+//   * reduce kernel: dk = (P0 + P1) + (P2 + P3) over the 4 parts.
+//
+// MFMA layout used throughout (32x32x16 BF16): operand lane l carries row/column l % 32 and
+// K elements 8 * (l / 32) .. +7; accumulator register i of lane l holds row
+// 8 * (i / 4) + 4 * (l / 32) + i % 4, column l % 32.  An accumulator used as the next MFMA's
+// operand therefore contributes, for K step st and lane half hf, the rows
+// 16 * st + 4 * hf + {0..3} and 16 * st + 8 + 4 * hf + {0..3}; the transposed LDS reads fetch
+// exactly those rows of the other operand, so both sides of each product agree on the K order.
+//
+// ds_read_b64_tr_b16 (measured lane layout): in each group of 16 lanes, lane 4*j + r points
+// at 4 consecutive 16-bit elements; lane 4*r + e receives element e of lanes r, 4+r, 8+r and
+// 12+r.  With lane 4*j + r pointing at row k0 + j, columns c0 + 4*r .. +3, lane i of the group
+// receives column c0 + i of rows k0 .. k0+3.
+
+#include "dsa_internal.h"
+#include "wave_ops.h"
+
+namespace dsa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWavesB = kBwdThreads / 64;
+constexpr int kTileBytes = kBwdKeyTile * kDim * 2;  // 16 KiB of keys (or of one query's q)
+constexpr int kRowBytes = kDim * 2;                 // one key row / one head row: 256 B
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kWaitVm = 0x0F70;  // s_waitcnt: wait on the vector memory counter only
+
+// dq/dw kernel LDS stage: key tile + one 64-key gradient row segment per wave
+constexpr int kDqStageBytes = kTileBytes + kWavesB * 256;
+// dk kernel LDS stage: q of the 4 streams' queries + their w rows + gradient row segments
+constexpr int kDkStageBytes = kDkStreams * (kTileBytes + 256 + 256);
+constexpr int kScratchInts = 16;
+
+static_assert(kBwdThreads == 512 && kBwdKeyTile == 64, "layout assumes 8 waves and 64-key tiles");
+static_assert(kDkStreams * 2 == kWavesB, "two waves (key halves) per query stream");
+static_assert(2 * kDkStageBytes >= kWavesB * 64 * 64 * 4, "stream sums fit in the stage memory");
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__device__ __forceinline__ int clampi(int64_t x, int lo, int hi) {
+  return (int)(x < lo ? lo : (x > hi ? hi : x));
+}
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+// g where S > 0 (as int32 the bits of a positive float are positive; +0, -0 and negatives are not)
+__device__ __forceinline__ float pass_pos(float s, float g) { return __float_as_int(s) > 0 ? g : 0.f; }
+
+__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 lds_b128(const unsigned char* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Two transposed 4-row reads -> one 8-element operand (rows k0..k0+3, then k0+8..k0+11).
+__device__ __forceinline__ bf16x8 lds_tr_pair(const unsigned char* p1, const unsigned char* p2) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p1));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p2));
+  const i16x8 v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Accumulator registers 8*jj .. 8*jj+7 as a BF16 operand (round to nearest even).
+__device__ __forceinline__ bf16x8 pack8(const f32x16& x, int jj) {
+  f32x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = x[8 * jj + e];
+  return __builtin_convertvector(v, bf16x8);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 4, voff, 0, 0, 0);
+}
+
+// Byte offset, inside a 64-row x 256-byte LDS tile, of 16-byte chunk `chunk` of row `row`
+// (chunks XOR-swizzled by the row's low 4 bits).
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 15)) << 4); }
+
+// Validates the segment tables (every thread of the block gets the flags): bit 0 = bad tables,
+// bit 1 = a segment longer than Lmax.  Block 0 records them in the status word.
+__device__ int table_flags(const BwdParams& p, int* scratch) {
+  const int tid = threadIdx.x;
+  if (tid == 0) scratch[10] = 0;
+  __syncthreads();
+  int flags = 0;
+  for (int b = tid; b <= p.B; b += kBwdThreads) {
+    const int cq = p.cu_q[b], ck = p.cu_k[b];
+    if (b == 0 && (cq != 0 || ck != 0)) flags |= 1;
+    if (b == p.B && (cq != p.T || ck != p.Tkv)) flags |= 1;
+    if (b < p.B) {
+      const int lq = p.cu_q[b + 1] - cq, lk = p.cu_k[b + 1] - ck;
+      if (lq < 0 || lk < 0) flags |= 1;
+      if (lk > p.Lmax) flags |= 2;
+    }
+  }
+  if (flags) atomicOr(&scratch[10], flags);
+  __syncthreads();
+  flags = scratch[10];
+  if (blockIdx.x == 0 && tid == 0 && flags)
+    atomicOr(p.ctrl + kCtrlStatus, ((flags & 1) ? kStatusBadSegments : 0u) | ((flags & 2) ? kStatusSeqlenBound : 0u));
+  return flags;
+}
+
+// Segment b and index inside it of unit u, units numbered segment by segment with count(b)
+// units in segment b; b = -1 if u is past the last unit.
+template <class CountFn>
+__device__ int locate_unit(int B, uint32_t u, CountFn count, int* scratch, int* idx) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid == 0) {
+    scratch[8] = -1;
+    scratch[9] = 0;
+  }
+  uint32_t carry = 0;
+  for (int base = 0; base < B; base += kBwdThreads) {
+    const int b = base + tid;
+    const uint32_t c = b < B ? count(b) : 0u;
+    const uint32_t inc = wave_incl_scan(c);
+    __syncthreads();
+    if (lane == 63) scratch[wv] = (int)inc;
+    __syncthreads();
+    uint32_t before = carry, total = carry;
+#pragma unroll
+    for (int i = 0; i < kWavesB; ++i) {
+      const uint32_t x = (uint32_t)scratch[i];
+      before += i < wv ? x : 0u;
+      total += x;
+    }
+    const uint32_t ex = before + inc - c;
+    if (c > 0 && u >= ex && u < ex + c) {
+      scratch[8] = b;
+      scratch[9] = (int)(u - ex);
+    }
+    carry = total;
+  }
+  __syncthreads();
+  *idx = scratch[9];
+  return scratch[8];
+}
+
+// ------------------------------------------------------------------------------------------
+// dq / dw
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int* const scratch = reinterpret_cast<int*>(smem + 2 * kDqStageBytes);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qi = wv >> 1, hg = wv & 1;
+  const int n = lane & 31, hf = lane >> 5;
+
+  if (table_flags(p, scratch) & 1) return;
+  int idx = 0;
+  const int b = locate_unit(p.B, blockIdx.x, [&](int s) -> uint32_t {
+    const int lq = p.cu_q[s + 1] - p.cu_q[s];
+    return (uint32_t)ceil_div(lq, kDqQueries);
+  }, scratch, &idx);
+  if (b < 0) return;
+
+  const int cq = p.cu_q[b], lq = p.cu_q[b + 1] - cq;
+  const int ck = p.cu_k[b], lk = min(p.cu_k[b + 1] - ck, p.Lmax);
+  const int64_t off = p.offs ? p.offs[b] : 0;
+  const int ti = ceil_div(lq, kDqQueries) - 1 - idx;   // most visible keys first
+  const int tq0 = ti * kDqQueries;
+  const int nq = min(kDqQueries, lq - tq0);
+  const int nmax = clampi(off + tq0 + nq, 0, lk);
+  const int ntk = ceil_div(nmax, kBwdKeyTile);
+  const bool qvalid = qi < nq;
+  const int64_t t = (int64_t)cq + tq0 + min(qi, nq - 1);
+  const int nt = __builtin_amdgcn_readfirstlane(qvalid ? clampi(off + tq0 + qi + 1, 0, lk) : 0);
+
+  // B operand of S^T = K . Q^T: column = head 32*hg + n, K elements d = 16*j + 8*hf .. +7
+  bf16x8 qf[8];
+  {
+    const uint16_t* qrow = p.q + (t * kHeads + 32 * hg + n) * kDim + 8 * hf;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qf[j] = qvalid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * j) : bf16x8{};
+  }
+
+  // keys at or past the segment's (bounded) end read as zero; gradients past the query's
+  // visible count read as zero, which masks every invisible pair
+  const __amdgpu_buffer_rsrc_t krs = rsrc(p.k + (int64_t)ck * kDim, lk * kRowBytes);
+  const __amdgpu_buffer_rsrc_t grs = rsrc(p.grad + t * p.ld, nt * 4);
+  auto stage = [&](int s) { return smem + s * kDqStageBytes; };
+  auto load_tile = [&](int s, int kt) {
+    unsigned char* const dst = stage(s);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int id = r * kWavesB + wv;
+      const int row = 4 * id + (lane >> 4), pos = lane & 15;
+      lds_load16(krs, dst + id * 1024, (kt * kBwdKeyTile + row) * kRowBytes + ((pos ^ (row & 15)) << 4));
+    }
+    lds_load4(grs, dst + kTileBytes + wv * 256, (kt * kBwdKeyTile + lane) * 4);
+  };
+  constexpr int kLoadsPerTile = 3;
+
+  // transposed-read offsets of the K operand of dq += G' . K: lane 4*jr + r of 16-lane group
+  // G reads rows 4*hf + jr (+8) and columns 32*nb + 16*(G&1) + 4*r .. +3
+  int trk1[4], trk2[4];
+  {
+    const int L = lane & 15, jr = L >> 2, r = L & 3, gs = (lane >> 4) & 1;
+    const int row1 = 4 * hf + jr, row2 = 8 + 4 * hf + jr;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int chunk = 4 * nb + 2 * gs + (r >> 1);
+      trk1[nb] = swz(row1, chunk) + 8 * (r & 1);
+      trk2[nb] = swz(row2, chunk) + 8 * (r & 1);
+    }
+  }
+
+  f32x16 dqa[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) dqa[nb] = f32x16{};
+  float dwa = 0.f;
+
+  if (ntk > 0) {
+    load_tile(0, 0);
+    for (int kt = 0; kt < ntk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < ntk) {
+        load_tile(cur ^ 1, kt + 1);
+        __builtin_amdgcn_s_waitcnt(kWaitVm | kLoadsPerTile);
+      } else {
+        __builtin_amdgcn_s_waitcnt(kWaitVm);
+      }
+      asm volatile("s_barrier" ::: "memory");
+      const unsigned char* const kb = stage(cur);
+      const float* const gb = reinterpret_cast<const float*>(kb + kTileBytes + wv * 256);
+
+      // S^T: row block rb = keys 32*rb + (accumulator rows), column = this lane's head
+      f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bf16x8 a0 = lds_b128(kb + swz(n, 2 * j + hf));
+        const bf16x8 a1 = lds_b128(kb + swz(32 + n, 2 * j + hf));
+        s0 = mfma(a0, qf[j], s0);
+        s1 = mfma(a1, qf[j], s1);
+      }
+      // epilogue: key of accumulator register i in row block rb = 32*rb + 8*(i/4) + 4*hf + i%4
+      bf16x8 ga[4];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        f32x16& sv = rb ? s1 : s0;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 gv = *reinterpret_cast<const f32x4*>(gb + 32 * rb + 8 * g4 + 4 * hf);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float e = sv[4 * g4 + c];
+            dwa = __builtin_fmaf(gv[c], relu_bits(e), dwa);
+            sv[4 * g4 + c] = pass_pos(e, gv[c]);
+          }
+        }
+        ga[2 * rb] = pack8(sv, 0);
+        ga[2 * rb + 1] = pack8(sv, 1);
+      }
+      // dq[h, d] += sum over the tile's keys of G'[h, key] * K[key, d]
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const bf16x8 bk = lds_tr_pair(kb + st * 16 * kRowBytes + trk1[nb], kb + st * 16 * kRowBytes + trk2[nb]);
+          dqa[nb] = mfma(ga[st], bk, dqa[nb]);
+        }
+      }
+      asm volatile("s_barrier" ::: "memory");
+    }
+  }
+
+  if (!qvalid) return;
+  // dq = w * accumulated sum; accumulator register i of dqa[nb]: head 32*hg + 8*(i/4) + 4*hf + i%4,
+  // dim 32*nb + n
+  const float* const wrow = p.w + t * kHeads + 32 * hg + 4 * hf;
+  float* const dqrow = p.dq + (t * kHeads + 32 * hg + 4 * hf) * kDim + n;
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) {
+    const f32x4 wv4 = *reinterpret_cast<const f32x4*>(wrow + 8 * g4);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        dqrow[(8 * g4 + c) * kDim + 32 * nb] = wv4[c] * dqa[nb][4 * g4 + c];
+    }
+  }
+  // dw: lanes n and n + 32 hold the same head's sums over disjoint keys
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(dwa), __float_as_uint(dwa), false, false);
+  const float dwt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  if (hf == 0) p.dw[t * kHeads + 32 * hg + n] = dwt;
+}
+
+// ------------------------------------------------------------------------------------------
+// dk partials
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dk_kernel(BwdParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int* const scratch = reinterpret_cast<int*>(smem + 2 * kDkStageBytes);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = wv & 1, rs = wv >> 1;
+  const int n = lane & 31, hf = lane >> 5;
+
+  if (table_flags(p, scratch) & 1) return;
+  int idx = 0;
+  const int b = locate_unit(p.B, blockIdx.x, [&](int s) -> uint32_t {
+    const int lk = p.cu_k[s + 1] - p.cu_k[s];
+    return (uint32_t)(ceil_div(lk, kBwdKeyTile) * kDkParts);
+  }, scratch, &idx);
+  if (b < 0) return;
+
+  const int cq = p.cu_q[b], lq = p.cu_q[b + 1] - cq;
+  const int ck = p.cu_k[b], lk_all = p.cu_k[b + 1] - ck;
+  const int lk = min(lk_all, p.Lmax);
+  const int64_t off = p.offs ? p.offs[b] : 0;
+  const int kt = idx / kDkParts, part = idx % kDkParts;   // first key tiles first
+  const int j0 = kt * kBwdKeyTile;
+  // queries that see key j0 (and so some key of the tile): off + i + 1 > j0
+  int i0 = 0, L = 0;
+  if (j0 < lk) {
+    i0 = clampi((int64_t)j0 - off, 0, lq);
+    L = lq - i0;
+  }
+  const int pbeg = i0 + (int)((int64_t)part * L / kDkParts);
+  const int pend = i0 + (int)((int64_t)(part + 1) * L / kDkParts);
+  const int iters = ceil_div(pend - pbeg, kDkStreams);
+
+  // B operand of S = Q . K^T: column = key j0 + 32*kh + n, K elements d = 16*j + 8*hf .. +7
+  bf16x8 kf[8];
+  {
+    const __amdgpu_buffer_rsrc_t krs = rsrc(p.k + (int64_t)ck * kDim, lk_all * kRowBytes);
+    const int voff = (j0 + 32 * kh + n) * kRowBytes + 16 * hf;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      kf[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, voff + 32 * j, 0, 0));
+  }
+
+  // stage layout: q of stream r at r * kTileBytes, w rows after the 4 q blocks, then gradients
+  auto qst = [&](int s, int r) { return smem + s * kDkStageBytes + r * kTileBytes; };
+  auto wst = [&](int s, int r) { return smem + s * kDkStageBytes + kDkStreams * kTileBytes + r * 256; };
+  auto gst = [&](int s, int r) { return smem + s * kDkStageBytes + kDkStreams * (kTileBytes + 256) + r * 256; };
+  // stream rs's query of iteration it (wave-uniform), its validity and visible key count
+  auto query_of = [&](int it, int64_t* tq, int* nvis) -> bool {
+    const int i = pbeg + kDkStreams * it + rs;
+    const bool ok = i < pend;
+    *tq = (int64_t)cq + (ok ? i : 0);
+    *nvis = ok ? clampi(off + i + 1, 0, lk) : 0;
+    return ok;
+  };
+  auto load_query = [&](int s, int it) {
+    int64_t tq;
+    int nv;
+    const bool ok = query_of(it, &tq, &nv);
+    const __amdgpu_buffer_rsrc_t qrs = rsrc(p.q + tq * (kHeads * kDim), ok ? kTileBytes : 0);
+    unsigned char* const dst = qst(s, rs);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int id = 8 * kh + c;
+      const int row = 4 * id + (lane >> 4), pos = lane & 15;
+      lds_load16(qrs, dst + id * 1024, row * kRowBytes + ((pos ^ (row & 15)) << 4));
+    }
+    if (kh == 0) {
+      lds_load4(rsrc(p.w + tq * kHeads, ok ? kHeads * 4 : 0), wst(s, rs), lane * 4);
+    } else {
+      lds_load4(rsrc(p.grad + tq * p.ld, nv * 4), gst(s, rs), (j0 + lane) * 4);
+    }
+  };
+  constexpr int kLoadsPerQuery = 9;
+
+  // transposed-read offsets of the Q^T operand of dk^T += Q^T . G'': rows (heads) 4*hf + jr
+  // (+8), columns (dims) 32*mb + 16*(G&1) + 4*r .. +3
+  int trq1[4], trq2[4];
+  {
+    const int L4 = lane & 15, jr = L4 >> 2, r = L4 & 3, gs = (lane >> 4) & 1;
+    const int row1 = 4 * hf + jr, row2 = 8 + 4 * hf + jr;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int chunk = 4 * mb + 2 * gs + (r >> 1);
+      trq1[mb] = swz(row1, chunk) + 8 * (r & 1);
+      trq2[mb] = swz(row2, chunk) + 8 * (r & 1);
+    }
+  }
+
+  f32x16 dka[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) dka[mb] = f32x16{};
+
+  if (iters > 0) {
+    load_query(0, 0);
+    for (int it = 0; it < iters; ++it) {
+      const int cur = it & 1;
+      if (it + 1 < iters) {
+        load_query(cur ^ 1, it + 1);
+        __builtin_amdgcn_s_waitcnt(kWaitVm | kLoadsPerQuery);
+      } else {
+        __builtin_amdgcn_s_waitcnt(kWaitVm);
+      }
+      asm volatile("s_barrier" ::: "memory");
+      const unsigned char* const qb = qst(cur, rs);
+      const float* const wb = reinterpret_cast<const float*>(wst(cur, rs));
+      const float gk = reinterpret_cast<const float*>(gst(cur, rs))[32 * kh + n];
+
+      // S: row block rb = heads 32*rb + (accumulator rows), column = this lane's key
+      f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bf16x8 a0 = lds_b128(qb + swz(n, 2 * j + hf));
+        const bf16x8 a1 = lds_b128(qb + swz(32 + n, 2 * j + hf));
+        s0 = mfma(a0, kf[j], s0);
+        s1 = mfma(a1, kf[j], s1);
+      }
+      // G'' = w[h] * g[key] where S > 0; head of register i in row block rb:
+      // 32*rb + 8*(i/4) + 4*hf + i%4
+      bf16x8 gb[4];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        f32x16& sv = rb ? s1 : s0;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 wv4 = *reinterpret_cast<const f32x4*>(wb + 32 * rb + 8 * g4 + 4 * hf);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) sv[4 * g4 + c] = pass_pos(sv[4 * g4 + c], wv4[c] * gk);
+        }
+        gb[2 * rb] = pack8(sv, 0);
+        gb[2 * rb + 1] = pack8(sv, 1);
+      }
+      // dk^T[d, key] += sum over heads of Q^T[d, h] * G''[h, key]
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const bf16x8 qa = lds_tr_pair(qb + st * 16 * kRowBytes + trq1[mb], qb + st * 16 * kRowBytes + trq2[mb]);
+          dka[mb] = mfma(qa, gb[st], dka[mb]);
+        }
+      }
+      asm volatile("s_barrier" ::: "memory");
+    }
+  }
+
+  // Streams' sums through LDS: wave (rs, kh) stores register v = 16*mb + i of lane l at
+  // float index ((rs * 2 + kh) * 64 + v) * 64 + l.  Register i of dka[mb] holds dim
+  // 32*mb + 8*(i/4) + 4*hf + i%4 of key 32*kh + n.
+  __syncthreads();
+  float* const red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[((wv * 64) + 16 * mb + i) * 64 + lane] = dka[mb][i];
+  __syncthreads();
+  // thread -> (key of the tile, 4 consecutive dims): 64 keys x 32 groups, 4 per thread
+  const int nkeys = min(kBwdKeyTile, lk_all - j0);
+  float* const out = p.part + ((int64_t)part * p.Tkv + ck + j0) * kDim;
+#pragma unroll
+  for (int rep = 0; rep < 4; ++rep) {
+    const int e = rep * kBwdThreads + tid;
+    const int key = e >> 5, dg = e & 31;       // dims 4*dg .. 4*dg+3
+    const int d0 = 4 * dg;
+    const int mb = d0 >> 5, g4 = (d0 >> 3) & 3, h2 = (d0 >> 2) & 1;
+    const int khk = key >> 5, l = (key & 31) + 32 * h2;
+    f32x4 v;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int reg = 16 * mb + 4 * g4 + c;
+      float x[kDkStreams];
+#pragma unroll
+      for (int r = 0; r < kDkStreams; ++r) x[r] = red[(((r * 2 + khk) * 64) + reg) * 64 + l];
+      v[c] = (x[0] + x[1]) + (x[2] + x[3]);
+    }
+    if (key < nkeys) *reinterpret_cast<f32x4*>(out + (int64_t)key * kDim + d0) = v;
+  }
+}
+
+// dk = (P0 + P1) + (P2 + P3), four floats per thread, grid-stride.
+__global__ __launch_bounds__(256) void bwd_dk_reduce_kernel(const float* __restrict__ part, float* __restrict__ dk,
+                                                            int64_t n4, int64_t stride, const uint32_t* ctrl) {
+  if (ctrl[kCtrlStatus] & kStatusBadSegments) return;
+  const f32x4* P = reinterpret_cast<const f32x4*>(part);
+  f32x4* out = reinterpret_cast<f32x4*>(dk);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    const f32x4 a = P[i], b = P[i + stride], c = P[i + 2 * stride], d = P[i + 3 * stride];
+    out[i] = (a + b) + (c + d);
+  }
+}
+
+}  // namespace
+
+size_t bwd_dq_smem_bytes() { return 2 * kDqStageBytes + kScratchInts * 4; }
+size_t bwd_dk_smem_bytes() { return 2 * kDkStageBytes + kScratchInts * 4; }
+
+hipError_t bwd_prepare() {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_dq_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bwd_dq_smem_bytes());
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_dk_kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bwd_dk_smem_bytes());
+}
+
+hipError_t launch_backward(const BwdParams& p, int dq_grid, int dk_grid, int cus, hipStream_t s,
+                           hipEvent_t between) {
+  if (dq_grid > 0) {
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(dq_grid), dim3(kBwdThreads), bwd_dq_smem_bytes(), s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (between) {
+    hipError_t e = hipEventRecord(between, s);
+    if (e != hipSuccess) return e;
+  }
+  if (dk_grid > 0) {
+    hipLaunchKernelGGL(bwd_dk_kernel, dim3(dk_grid), dim3(kBwdThreads), bwd_dk_smem_bytes(), s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n4 = (int64_t)p.Tkv * (kDim / 4);
+    const int64_t blocks = (n4 + 255) / 256;
+    const int grid = (int)(blocks < (int64_t)cus * 8 ? blocks : (int64_t)cus * 8);
+    hipLaunchKernelGGL(bwd_dk_reduce_kernel, dim3(grid), dim3(256), 0, s, p.part, p.dk, n4, n4, p.ctrl);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace dsa

@@ -39,6 +39,7 @@ const DeviceInfo* device_info() {
     if (dsa::score_prepare(dsa::score_smem_limit()) != hipSuccess) return;
     int bpc = 0;
     if (dsa::score_occupancy(&bpc, dsa::score_smem_limit()) != hipSuccess || bpc < 1) return;
+    if (dsa::bwd_prepare() != hipSuccess) return;
     info.score_blocks_per_cu = bpc;
     info.ok = true;
     g_info[dev] = info;
@@ -315,6 +316,75 @@ int dsa_indexer_profiler_read(dsa_indexer_profiler* prof, double* score_ms, doub
   *calls = prof->used;
   prof->used = 0;
   return DSA_OK;
+}
+
+size_t dsa_indexer_backward_workspace_size(const dsa_indexer_shape* shape) {
+  if (check_shape(shape) != DSA_OK) return 0;
+  return (size_t)dsa::kCtrlBytes + (size_t)dsa::kDkParts * (size_t)shape->total_k * dsa::kDim * 4u;
+}
+
+int dsa_indexer_backward_ex(const dsa_indexer_shape* shape, const void* q, const void* k,
+                            const float* w, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, const int32_t* q_pos_offsets,
+                            const float* grad_scores, int64_t ld_grad, float* dq, float* dk,
+                            float* dw, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                            dsa_indexer_profiler* profiler) {
+  int rc = check_common(shape, q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets, workspace);
+  if (rc) return rc;
+  const bool has_q = shape->total_q > 0, has_k = shape->total_k > 0;
+  if ((has_q && (!grad_scores || !dq || !dw)) || (has_k && !dk)) return DSA_ERR_NULL;
+  if ((grad_scores && !aligned16(grad_scores)) || (dq && !aligned16(dq)) || (dk && !aligned16(dk)) ||
+      (dw && !aligned16(dw)))
+    return DSA_ERR_ALIGN;
+  if (ld_grad < lmax_of(shape) || (ld_grad & 3)) return DSA_ERR_SHAPE;
+  if (workspace_bytes < dsa_indexer_backward_workspace_size(shape)) return DSA_ERR_WORKSPACE;
+  const DeviceInfo* dev = device_info();
+  if (!dev) return DSA_ERR_DEVICE;
+  if (profiler && profiler->used >= profiler->capacity) return DSA_ERR_SHAPE;
+  if (!has_q && !has_k) return DSA_OK;
+
+  dsa::BwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.w = w;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.offs = q_pos_offsets;
+  p.grad = grad_scores;
+  p.ld = ld_grad;
+  p.dq = dq;
+  p.dk = dk;
+  p.dw = dw;
+  p.part = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + dsa::kCtrlBytes);
+  p.ctrl = static_cast<uint32_t*>(workspace);
+  p.B = shape->num_segments;
+  p.T = shape->total_q;
+  p.Tkv = shape->total_k;
+  p.Lmax = (int32_t)lmax_of(shape);
+  // unit counts are at most these bounds; blocks past the last unit leave at once
+  const int64_t dq_grid = has_q ? (int64_t)(shape->total_q + dsa::kDqQueries - 1) / dsa::kDqQueries + shape->num_segments : 0;
+  const int64_t dk_grid = has_k ? ((int64_t)(shape->total_k + dsa::kBwdKeyTile - 1) / dsa::kBwdKeyTile + shape->num_segments) * dsa::kDkParts : 0;
+  if (dq_grid > INT32_MAX || dk_grid > INT32_MAX) return DSA_ERR_SHAPE;
+
+  hipEvent_t* ev = profiler ? &profiler->ev[3 * profiler->used] : nullptr;
+  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return DSA_ERR_LAUNCH;
+  if (dsa::launch_backward(p, (int)dq_grid, (int)dk_grid, dev->cus, stream, ev ? ev[1] : nullptr) != hipSuccess)
+    return DSA_ERR_LAUNCH;
+  if (ev) {
+    if (hipEventRecord(ev[2], stream) != hipSuccess) return DSA_ERR_LAUNCH;
+    profiler->used++;
+  }
+  return DSA_OK;
+}
+
+int dsa_indexer_backward(const dsa_indexer_shape* shape, const void* q, const void* k,
+                         const float* w, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                         const int32_t* q_pos_offsets, const float* grad_scores, int64_t ld_grad,
+                         float* dq, float* dk, float* dw, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  return dsa_indexer_backward_ex(shape, q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets,
+                                 grad_scores, ld_grad, dq, dk, dw, workspace, workspace_bytes,
+                                 stream, nullptr);
 }
 
 int dsa_indexer_read_status(const void* workspace, hipStream_t stream, uint32_t* status,

@@ -62,6 +62,37 @@ struct SelectParams {
   int32_t B, T, Tkv, Lmax, topk;
 };
 
+// Backward of the scores (dq, dk, dw).
+constexpr int kBwdThreads = 512;
+constexpr int kBwdKeyTile = 64;  // keys per LDS tile
+constexpr int kDqQueries = 4;    // queries per dq unit (two waves per query, 32 heads each)
+constexpr int kDkStreams = 4;    // query streams per dk unit
+constexpr int kDkParts = 4;      // query parts per key tile; dk = fixed tree over the parts
+
+struct BwdParams {
+  const uint16_t* q;  // bf16 [T, H, D]
+  const uint16_t* k;  // bf16 [Tkv, D]
+  const float* w;     // fp32 [T, H]
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* offs;  // may be null
+  const float* grad;    // fp32 rows of stride ld: dL/dI of the visible keys
+  int64_t ld;
+  float* dq;    // fp32 [T, H, D]
+  float* dk;    // fp32 [Tkv, D]
+  float* dw;    // fp32 [T, H]
+  float* part;  // fp32 [kDkParts, Tkv, D] partial key gradients
+  uint32_t* ctrl;
+  int32_t B, T, Tkv, Lmax;
+};
+
+size_t bwd_dq_smem_bytes();
+size_t bwd_dk_smem_bytes();
+hipError_t bwd_prepare();
+// `between` (may be null) is recorded after the dq/dw kernel.
+hipError_t launch_backward(const BwdParams& p, int dq_grid, int dk_grid, int cus, hipStream_t s,
+                           hipEvent_t between);
+
 // Dynamic LDS bytes of the score kernel for a tile table of `max_tiles` entries.
 size_t score_smem_bytes(int B, int max_tiles);
 size_t score_smem_limit();

@@ -40,6 +40,9 @@ EXPORTED_SYMBOLS = (
     "dsa_indexer_profiler_read_calls",
     "dsa_indexer_topk_ex",
     "dsa_indexer_read_status",
+    "dsa_indexer_backward_workspace_size",
+    "dsa_indexer_backward",
+    "dsa_indexer_backward_ex",
 )
 
 
@@ -100,6 +103,12 @@ def lib():
         L.dsa_indexer_read_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32),
                                               ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32)]
         L.dsa_indexer_read_status.restype = ctypes.c_int
+        L.dsa_indexer_backward_workspace_size.argtypes = [sp]
+        L.dsa_indexer_backward_workspace_size.restype = sz
+        L.dsa_indexer_backward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
+        L.dsa_indexer_backward.restype = ctypes.c_int
+        L.dsa_indexer_backward_ex.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp, vp]
+        L.dsa_indexer_backward_ex.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -271,6 +280,51 @@ def scores(q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets=None, max_seqlen_k
                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
     _check(rc, "dsa_indexer_scores")
     return out
+
+
+def backward_workspace_size(T: int, Tkv: int, B: int, max_seqlen_k: int = 0) -> int:
+    s = make_shape(T, Tkv, B, max_seqlen_k)
+    n = lib().dsa_indexer_backward_workspace_size(ctypes.byref(s))
+    if n == 0:
+        raise DsaError(-3, "backward_workspace_size")
+    return int(n)
+
+
+def backward(q, k, w, cu_seqlens_q, cu_seqlens_k, grad, q_pos_offsets=None, max_seqlen_k: int = 0,
+             workspace: Optional[torch.Tensor] = None, dq: Optional[torch.Tensor] = None,
+             dk: Optional[torch.Tensor] = None, dw: Optional[torch.Tensor] = None,
+             profiler: Optional[Profiler] = None):
+    """Gradients (dq fp32 [T,H,D], dk fp32 [Tkv,D], dw fp32 [T,H]) of the scores.
+
+    grad: fp32 [T, ld] in the layout `scores` returns (column j of row t = key first_t + j;
+    only the visible columns are read).
+    """
+    dev, T, Tkv, B = _inputs(q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets)
+    if grad.dtype != torch.float32 or grad.dim() != 2 or grad.shape[0] != T or not grad.is_contiguous() \
+            or grad.device != dev:
+        raise ValueError("grad must be a contiguous fp32 [T, ld] tensor on the inputs' device")
+    if dq is None:
+        dq = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.empty((Tkv, D), dtype=torch.float32, device=dev)
+    if dw is None:
+        dw = torch.empty((T, H), dtype=torch.float32, device=dev)
+    _require(dq, "dq", torch.float32, (T, H, D), dev)
+    _require(dk, "dk", torch.float32, (Tkv, D), dev)
+    _require(dw, "dw", torch.float32, (T, H), dev)
+    if workspace is None:
+        workspace = torch.empty(backward_workspace_size(T, Tkv, B, max_seqlen_k), dtype=torch.uint8, device=dev)
+        workspace_init(workspace)
+    shape = make_shape(T, Tkv, B, max_seqlen_k)
+    args = (ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(w), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+            _ptr(q_pos_offsets), _ptr(grad), int(grad.shape[1]), _ptr(dq), _ptr(dk), _ptr(dw),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+    if profiler is None:
+        rc = lib().dsa_indexer_backward(*args)
+    else:
+        rc = lib().dsa_indexer_backward_ex(*args, profiler.handle)
+    _check(rc, "dsa_indexer_backward")
+    return dq, dk, dw
 
 
 def read_status(workspace: torch.Tensor):

@@ -132,6 +132,37 @@ int dsa_indexer_scores(const dsa_indexer_shape* shape, const void* q, const void
                        const int32_t* q_pos_offsets, float* out_scores, int64_t ld_out,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Backward of the scores ("indexer logits backward", named beside the logits kernels in the
+ * vendoring commit message of flashinfer PR #8691, which also fixes its determinism rules: no
+ * floating-point atomics, key-side gradients summed from FP32 partials in a fixed tree).
+ * With S[t,h,s] = q[t,h,:] . k[s,:] and g[t,j] = grad_scores[t * ld_grad + j], the upstream
+ * gradient of I[t, cu_seqlens_k[b] + j] for the visible j < n_t (other elements are not read):
+ *     dw[t,h]    = sum_j g[t,j] * max(0, S[t,h,s])
+ *     dq[t,h,:]  = w[t,h] * sum_j g[t,j] * [S[t,h,s] > 0] * k[s,:]
+ *     dk[s,:]    = sum over the queries t that see s, sum_h w[t,h] * g[t,j] * [S[t,h,s] > 0] * q[t,h,:]
+ * (the ReLU's derivative at 0 is 0).  S is the FP32 product of the forward; the gradient
+ * factors entering the matrix cores (g for dq, w * g for dk) are rounded to BF16, all sums
+ * are FP32.
+ *   grad_scores    fp32 rows of stride ld_grad (>= max_seqlen_k, multiple of 4): the layout
+ *                  that dsa_indexer_scores writes
+ *   dq             fp32 [T, 64, 128], dk fp32 [Tkv, 128], dw fp32 [T, 64]: fully overwritten
+ *                  (keys no query sees and queries that see no key get zeros)
+ *   workspace      >= dsa_indexer_backward_workspace_size(shape) bytes, initialised once
+ *                  (dsa_indexer_workspace_init); holds the status word and 4 FP32 partial
+ *                  key gradients per key
+ * Bit-reproducible: every sum has a fixed order that depends only on the segment tables.
+ * Invalid device tables (DSA_STATUS_BAD_SEGMENTS) leave the outputs untouched; a segment
+ * longer than max_seqlen_k is flagged (DSA_STATUS_SEQLEN_BOUND) and its keys past the bound
+ * get dk = 0, as in the forward.
+ */
+size_t dsa_indexer_backward_workspace_size(const dsa_indexer_shape* shape);
+int dsa_indexer_backward(const dsa_indexer_shape* shape, const void* q, const void* k,
+                         const float* w, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                         const int32_t* q_pos_offsets, const float* grad_scores, int64_t ld_grad,
+                         float* dq, float* dk, float* dw, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
 /* Text of a DSA_ERR_* code. */
 const char* dsa_indexer_status_string(int code);
 
@@ -173,6 +204,17 @@ int dsa_indexer_topk_ex(const dsa_indexer_shape* shape, const void* q, const voi
                         float* out_scores, void* workspace, size_t workspace_bytes,
                         hipStream_t stream, const dsa_indexer_tuning* tuning,
                         dsa_indexer_profiler* profiler);
+
+/*
+ * dsa_indexer_backward with an optional profiler: for backward calls the two figures a
+ * profiler read returns are the dq/dw kernel and the dk kernels (partials + fixed-tree sum).
+ */
+int dsa_indexer_backward_ex(const dsa_indexer_shape* shape, const void* q, const void* k,
+                            const float* w, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, const int32_t* q_pos_offsets,
+                            const float* grad_scores, int64_t ld_grad, float* dq, float* dk,
+                            float* dw, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                            dsa_indexer_profiler* profiler);
 
 /*
  * Test helper: synchronise `stream`, then copy the control block's status word and the two

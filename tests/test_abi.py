@@ -116,3 +116,24 @@ def test_profiler_argument_errors():
     assert L.dsa_indexer_profiler_create(0, ctypes.byref(h)) == -3
     assert L.dsa_indexer_profiler_read(None, None, None, None) == -1
     assert L.dsa_indexer_profiler_read_calls(None, None, None, 0, None) == -1
+
+
+def test_backward_argument_errors():
+    L = ix.lib()
+    V = ctypes.c_void_p
+    s = ix.make_shape(16, 64, 1, 64)
+    assert ix.backward_workspace_size(16, 64, 1) == 256 + 4 * 64 * 128 * 4
+    q, k, w, cq, ck, _, g, dq, ws = GOOD
+    dk, dw = 0x90000, 0xA0000
+
+    def call(grad=g, ld=64, dq_=dq, dk_=dk, dw_=dw, ws_bytes=1 << 40, shape=s):
+        return L.dsa_indexer_backward(ctypes.byref(shape), V(q), V(k), V(w), V(cq), V(ck), None, V(grad), ld,
+                                      V(dq_), V(dk_), V(dw_), V(ws), ws_bytes, None)
+    assert call(grad=None) == -1
+    assert call(dk_=None) == -1
+    assert call(dw_=0xA0004) == -2
+    assert call(ld=60) == -3                     # below max_seqlen_k
+    assert call(ld=66) == -3                     # not a multiple of 4
+    assert call(ws_bytes=1000) == -4
+    no_k = ix.make_shape(16, 0, 1, 64)
+    assert call(dk_=None, shape=no_k) in (0, -6)  # no keys: dk may be NULL
