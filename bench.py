@@ -142,6 +142,119 @@ def cpu_baseline(wl, ids, sc, budget_s):
                       f"{el:.1f} s, FP64 NumPy, host cpu_count={os.cpu_count()} ({cpu})"}, ok
 
 
+def cpu_baseline_backward(wl, grad, dq, dw, budget_s):
+    """FP64 oracle backward, one query row at a time, until the budget is spent; checks those rows' dq, dw."""
+    import numpy as np
+    from oracle import dsa_oracle as O
+    from tests.parity import backward_row_bounds
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    q64, k64, w64 = O.from_torch(wl.q, wl.k, wl.w)
+    cu_q, cu_k = wl.cu_seqlens_q.numpy(), wl.cu_seqlens_k.numpy()
+    offs = None if wl.q_pos_offsets is None else wl.q_pos_offsets.numpy()
+    order = np.random.default_rng(0).permutation(wl.T).tolist()
+    done, ok = 0, True
+    t0 = time.perf_counter()
+    for t in order:
+        first, n = O.visible(cu_q, cu_k, offs, t)
+        g = grad[t, :n].astype(np.float64)
+        rq, rw, _ = O.row_backward(q64, k64, w64, t, first, n, g)
+        if n:
+            bq, bw, _, _ = backward_row_bounds(q64, k64, w64, g, t, first, n)
+            if (np.abs(dq[t] - rq) > bq).any() or (np.abs(dw[t] - rw) > bw).any():
+                ok = False
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    what = "all" if done == wl.T else "a seeded random sample of"
+    return {"value": done / el, "unit": "queries/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{what} {done} of {wl.T} query rows, one oracle row_backward call per row (dq, dw and the "
+                      f"row's dk terms; the GPU's dq and dw of those rows checked against the derived error "
+                      f"bound), {el:.1f} s, FP64 NumPy, host cpu_count={os.cpu_count()}"}, ok
+
+
+def bench_backward(args):
+    """One step = one dsa_indexer_backward call (dq/dw kernel + dk kernels) over the whole workload."""
+    import torch
+    from deterministic_score_top_amd import indexer as ix
+    from deterministic_score_top_amd import workloads as W
+
+    wl = W.make(args.config)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = wl.max_seqlen_k if wl.max_seqlen_k > 0 else wl.Tkv
+    ld = (L + 3) // 4 * 4
+    print(f"bench: backward {args.config} T={wl.T} Tkv={wl.Tkv} B={wl.B}", file=sys.stderr, flush=True)
+    grad_h = W.draw_grad(wl.T, ld, seed=1)
+    q, k, w = wl.q.to(dev), wl.k.to(dev), wl.w.to(dev)
+    cq, ck = wl.cu_seqlens_q.to(dev), wl.cu_seqlens_k.to(dev)
+    offs = None if wl.q_pos_offsets is None else wl.q_pos_offsets.to(dev)
+    grad = grad_h.to(dev)
+    ws = torch.empty(ix.backward_workspace_size(wl.T, wl.Tkv, wl.B, wl.max_seqlen_k), dtype=torch.uint8, device=dev)
+    ix.workspace_init(ws)
+    dq = torch.empty((wl.T, 64, 128), dtype=torch.float32, device=dev)
+    dk = torch.empty((wl.Tkv, 128), dtype=torch.float32, device=dev)
+    dw = torch.empty((wl.T, 64), dtype=torch.float32, device=dev)
+    call = dict(max_seqlen_k=wl.max_seqlen_k, workspace=ws, dq=dq, dk=dk, dw=dw)
+    for _ in range(args.warmup):
+        ix.backward(q, k, w, cq, ck, grad, offs, **call)
+    prof = ix.Profiler(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ix.backward(q, k, w, cq, ck, grad, offs, profiler=prof, **call)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    per_q, per_k = prof.read_calls()
+    prof.close()
+    st = ix.read_status(ws)
+    if st[0] != 0:
+        print(f"bench: workspace status {st}", file=sys.stderr)
+    pairs = visible_pairs(wl)
+    ms = el * 1000.0 / args.steps
+    q_ms, k_ms = sum(per_q) / len(per_q), sum(per_k) / len(per_k)
+    # each kernel recomputes S (2HD per pair) and forms one gradient product (2HD per pair);
+    # the call's algorithmic minimum is S once plus the two gradient products
+    kern_flop = 2 * FLOP_PER_PAIR * pairs
+    call_flop = 3 * FLOP_PER_PAIR * pairs
+    dom_name, dom_ms = ("bwd_dq_kernel", q_ms) if q_ms >= k_ms else ("bwd_dk_kernel + reduce", k_ms)
+    eff_dom = kern_flop / (dom_ms * 1e-3) / 1e12
+    eff_call = call_flop / (ms * 1e-3) / 1e12
+    print(f"bench: backward {ms:.4f} ms/call, dq/dw kernel {q_ms:.4f} ms, dk kernels {k_ms:.4f} ms",
+          file=sys.stderr, flush=True)
+    line = {
+        "metric": "indexer backward queries/s + effective TFLOP/s (frac of BF16 MFMA peak)",
+        "value": wl.T / (ms * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.config, "T": wl.T, "Tkv": wl.Tkv, "segments": wl.B, "heads": 64,
+                   "head_dim": 128, "visible_pairs": pairs, "grad": "N(0,1) FP32, seed 1"},
+        "effective_tflops_call": eff_call,
+        "flop_per_pair_call": 3 * FLOP_PER_PAIR,
+        "dq_kernel_ms": q_ms,
+        "dk_kernels_ms": k_ms,
+        "roofline": {"bound": "mfma", "kernel": dom_name, "achieved": eff_dom, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": eff_dom / PEAK_BF16_TFLOPS, "flop_per_pair": 2 * FLOP_PER_PAIR,
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"], line["parity_sample_ok"] = cpu_baseline_backward(
+            wl, grad_h.numpy(), dq.cpu().numpy(), dw.cpu().numpy(), args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -159,6 +272,8 @@ def main():
                          "T / median per-call GPU time")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of known size (counter calibration)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward of the scores (dq, dk, dw) instead of the top-k call")
     ap.add_argument("--ingest-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write the score-kernel traffic record from rocprofv3 --pmc output directories")
     args = ap.parse_args()
@@ -172,6 +287,10 @@ def main():
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the scan shards by queries; a multi-GPU driver is not part of this library)", file=sys.stderr)
         sys.exit(2)
+
+    if args.backward:
+        bench_backward(args)
+        return
 
     import torch
     from deterministic_score_top_amd import indexer as ix

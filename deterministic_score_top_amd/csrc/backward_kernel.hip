@@ -12,18 +12,22 @@
 //
 // Three kernels, no atomics on any gradient, every sum in a fixed order:
 //   * dq/dw kernel, query-major: a unit is 4 consecutive queries of one segment; wave w takes
-//     query w/2 and heads 32*(w%2) .. +31.  Per 64-key tile it recomputes S^T = K . Q^T
+//     query w/2 and heads 32*(w%2) .. +31.  Key tiles land in LDS two ahead (three buffers,
+//     one barrier per tile).  Per 64-key tile it recomputes S^T = K . Q^T
 //     (v_mfma_f32_32x32x16_bf16, K tile from LDS, Q in VGPRs), forms dw partials in FP32 and
 //     the BF16 operand G' = g * [S > 0] (w is factored out of the key sum and applied once at
 //     the end), and accumulates dq += G' . K with the K operand read key-major from the same
 //     LDS tile by ds_read_b64_tr_b16.
-//   * dk kernel, key-major: a unit is (one 64-key tile, one of 4 parts of the queries that see
-//     it).  Wave w takes keys 32*(w%2) .. +31 of the tile and query stream w/2; the 4 streams
-//     take the part's queries in turn.  Per query: S = Q . K^T (K in VGPRs for the whole
-//     unit, Q from LDS), the BF16 operand G'' = w * g * [S > 0], and dk^T += Q^T . G'' with
-//     the Q^T operand read head-major from LDS by ds_read_b64_tr_b16.  The 4 streams' FP32
-//     sums are added in a fixed tree ((0 + 1) + (2 + 3)) and stored as the unit's partial.
-//   * reduce kernel: dk = (P0 + P1) + (P2 + P3) over the 4 parts.
+//   * dk kernel, key-major: a unit is (a block of 256 keys, one of P parts of the queries that
+//     see its first key); wave w owns keys 32*w .. +31 of the block and all 8 waves walk the
+//     part's queries together, one query per step.  Per query: S = Q . K^T (K in VGPRs for
+//     the whole unit, Q from LDS), the BF16 operand G'' = w * g * [S > 0], and
+//     dk^T += Q^T . G'' with the Q^T operand read head-major from LDS by ds_read_b64_tr_b16.
+//     A query's 16 KiB q block thus serves 256 keys per load.  P (1, 2, 4, 8 or 16) depends
+//     only on the number of keys: enough parts for about 512 units.  With P = 1 the unit
+//     writes dk itself; otherwise it writes an FP32 partial.
+//   * reduce kernel (P > 1): dk = the P partials added in a fixed pairwise tree
+//     ((P0 + P1) + (P2 + P3)) + ...
 //
 // MFMA layout used throughout (32x32x16 BF16): operand lane l carries row/column l % 32 and
 // K elements 8 * (l / 32) .. +7; accumulator register i of lane l holds row
@@ -58,13 +62,16 @@ constexpr int kWaitVm = 0x0F70;  // s_waitcnt: wait on the vector memory counter
 
 // dq/dw kernel LDS stage: key tile + one 64-key gradient row segment per wave
 constexpr int kDqStageBytes = kTileBytes + kWavesB * 256;
-// dk kernel LDS stage: q of the 4 streams' queries + their w rows + gradient row segments
-constexpr int kDkStageBytes = kDkStreams * (kTileBytes + 256 + 256);
+constexpr int kStages = 3;
+// dk kernel LDS stage: q of one query, the gradients of the unit's keys, w, and a landing
+// area for the waves that have no third load
+constexpr int kDkStageBytes = kTileBytes + kDkKeys * 4 + 256 + 256;
+constexpr int kDkOutStride = 132;  // floats per key row when the unit's sums leave through LDS
+constexpr int kDkOutBytes = kWavesB * 32 * kDkOutStride * 4;
 constexpr int kScratchInts = 16;
 
 static_assert(kBwdThreads == 512 && kBwdKeyTile == 64, "layout assumes 8 waves and 64-key tiles");
-static_assert(kDkStreams * 2 == kWavesB, "two waves (key halves) per query stream");
-static_assert(2 * kDkStageBytes >= kWavesB * 64 * 64 * 4, "stream sums fit in the stage memory");
+static_assert(kDkKeys == 32 * kWavesB, "32 keys per wave in the dk kernel");
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 __device__ __forceinline__ int clampi(int64_t x, int lo, int hi) {
@@ -178,7 +185,7 @@ __device__ int locate_unit(int B, uint32_t u, CountFn count, int* scratch, int* 
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  int* const scratch = reinterpret_cast<int*>(smem + 2 * kDqStageBytes);
+  int* const scratch = reinterpret_cast<int*>(smem + kStages * kDqStageBytes);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qi = wv >> 1, hg = wv & 1;
@@ -250,16 +257,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p) {
 
   if (ntk > 0) {
     load_tile(0, 0);
+    if (ntk > 1) load_tile(1, 1);
+    if (ntk > 1) __builtin_amdgcn_s_waitcnt(kWaitVm | kLoadsPerTile);
+    else __builtin_amdgcn_s_waitcnt(kWaitVm);
+    asm volatile("s_barrier" ::: "memory");
     for (int kt = 0; kt < ntk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < ntk) {
-        load_tile(cur ^ 1, kt + 1);
-        __builtin_amdgcn_s_waitcnt(kWaitVm | kLoadsPerTile);
-      } else {
-        __builtin_amdgcn_s_waitcnt(kWaitVm);
-      }
-      asm volatile("s_barrier" ::: "memory");
-      const unsigned char* const kb = stage(cur);
+      // tile kt + 2 goes to the buffer every wave finished reading before the last barrier
+      if (kt + 2 < ntk) load_tile((kt + 2) % kStages, kt + 2);
+      const unsigned char* const kb = stage(kt % kStages);
       const float* const gb = reinterpret_cast<const float*>(kb + kTileBytes + wv * 256);
 
       // S^T: row block rb = keys 32*rb + (accumulator rows), column = this lane's head
@@ -298,6 +303,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p) {
           dqa[nb] = mfma(ga[st], bk, dqa[nb]);
         }
       }
+      // tile kt + 1 must have landed (only tile kt + 2's loads may still be in flight)
+      if (kt + 2 < ntk) __builtin_amdgcn_s_waitcnt(kWaitVm | kLoadsPerTile);
+      else __builtin_amdgcn_s_waitcnt(kWaitVm);
       asm volatile("s_barrier" ::: "memory");
     }
   }
@@ -324,21 +332,22 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------------------------------------
-// dk partials
+// dk (or its partials)
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dk_kernel(BwdParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  int* const scratch = reinterpret_cast<int*>(smem + 2 * kDkStageBytes);
+  constexpr int kStageArea = kStages * kDkStageBytes > kDkOutBytes ? kStages * kDkStageBytes : kDkOutBytes;
+  int* const scratch = reinterpret_cast<int*>(smem + kStageArea);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kh = wv & 1, rs = wv >> 1;
   const int n = lane & 31, hf = lane >> 5;
+  const int parts = p.dk_parts;
 
   if (table_flags(p, scratch) & 1) return;
   int idx = 0;
   const int b = locate_unit(p.B, blockIdx.x, [&](int s) -> uint32_t {
     const int lk = p.cu_k[s + 1] - p.cu_k[s];
-    return (uint32_t)(ceil_div(lk, kBwdKeyTile) * kDkParts);
+    return (uint32_t)(ceil_div(lk, kDkKeys) * parts);
   }, scratch, &idx);
   if (b < 0) return;
 
@@ -346,59 +355,51 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dk_kernel(BwdParams p) {
   const int ck = p.cu_k[b], lk_all = p.cu_k[b + 1] - ck;
   const int lk = min(lk_all, p.Lmax);
   const int64_t off = p.offs ? p.offs[b] : 0;
-  const int kt = idx / kDkParts, part = idx % kDkParts;   // first key tiles first
-  const int j0 = kt * kBwdKeyTile;
-  // queries that see key j0 (and so some key of the tile): off + i + 1 > j0
+  const int kb = idx / parts, part = idx % parts;   // first key blocks (most queries) first
+  const int j0 = kb * kDkKeys;
+  // queries that see key j0 (the block's first key): off + i + 1 > j0
   int i0 = 0, L = 0;
   if (j0 < lk) {
     i0 = clampi((int64_t)j0 - off, 0, lq);
     L = lq - i0;
   }
-  const int pbeg = i0 + (int)((int64_t)part * L / kDkParts);
-  const int pend = i0 + (int)((int64_t)(part + 1) * L / kDkParts);
-  const int iters = ceil_div(pend - pbeg, kDkStreams);
+  const int pbeg = i0 + (int)((int64_t)part * L / parts);
+  const int iters = i0 + (int)((int64_t)(part + 1) * L / parts) - pbeg;
 
-  // B operand of S = Q . K^T: column = key j0 + 32*kh + n, K elements d = 16*j + 8*hf .. +7
+  // B operand of S = Q . K^T: column = key j0 + 32*wv + n, K elements d = 16*j + 8*hf .. +7
   bf16x8 kf[8];
   {
     const __amdgpu_buffer_rsrc_t krs = rsrc(p.k + (int64_t)ck * kDim, lk_all * kRowBytes);
-    const int voff = (j0 + 32 * kh + n) * kRowBytes + 16 * hf;
+    const int voff = (j0 + 32 * wv + n) * kRowBytes + 16 * hf;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       kf[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, voff + 32 * j, 0, 0));
   }
 
-  // stage layout: q of stream r at r * kTileBytes, w rows after the 4 q blocks, then gradients
-  auto qst = [&](int s, int r) { return smem + s * kDkStageBytes + r * kTileBytes; };
-  auto wst = [&](int s, int r) { return smem + s * kDkStageBytes + kDkStreams * kTileBytes + r * 256; };
-  auto gst = [&](int s, int r) { return smem + s * kDkStageBytes + kDkStreams * (kTileBytes + 256) + r * 256; };
-  // stream rs's query of iteration it (wave-uniform), its validity and visible key count
-  auto query_of = [&](int it, int64_t* tq, int* nvis) -> bool {
-    const int i = pbeg + kDkStreams * it + rs;
-    const bool ok = i < pend;
-    *tq = (int64_t)cq + (ok ? i : 0);
-    *nvis = ok ? clampi(off + i + 1, 0, lk) : 0;
-    return ok;
-  };
+  // stage layout: q (16 KiB) | gradients of the 256 keys | w | landing area
+  auto qst = [&](int s) { return smem + s * kDkStageBytes; };
+  auto gst = [&](int s) { return smem + s * kDkStageBytes + kTileBytes; };
+  auto wst = [&](int s) { return smem + s * kDkStageBytes + kTileBytes + kDkKeys * 4; };
+  auto dst_ = [&](int s) { return smem + s * kDkStageBytes + kTileBytes + kDkKeys * 4 + 256; };
+  // every wave issues 3 loads per query: 2 x 1 KiB of q, then gradients (waves 0-3), w (wave 4)
+  // or nothing useful (a zero-length load into the landing area)
   auto load_query = [&](int s, int it) {
-    int64_t tq;
-    int nv;
-    const bool ok = query_of(it, &tq, &nv);
-    const __amdgpu_buffer_rsrc_t qrs = rsrc(p.q + tq * (kHeads * kDim), ok ? kTileBytes : 0);
-    unsigned char* const dst = qst(s, rs);
+    const int i = pbeg + it;
+    const int64_t t = (int64_t)cq + i;
+    const int nv = clampi(off + i + 1, 0, lk);
+    const __amdgpu_buffer_rsrc_t qrs = rsrc(p.q + t * (kHeads * kDim), kTileBytes);
+    unsigned char* const qd = qst(s);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int id = 8 * kh + c;
+    for (int r = 0; r < 2; ++r) {
+      const int id = r * kWavesB + wv;
       const int row = 4 * id + (lane >> 4), pos = lane & 15;
-      lds_load16(qrs, dst + id * 1024, row * kRowBytes + ((pos ^ (row & 15)) << 4));
+      lds_load16(qrs, qd + id * 1024, row * kRowBytes + ((pos ^ (row & 15)) << 4));
     }
-    if (kh == 0) {
-      lds_load4(rsrc(p.w + tq * kHeads, ok ? kHeads * 4 : 0), wst(s, rs), lane * 4);
-    } else {
-      lds_load4(rsrc(p.grad + tq * p.ld, nv * 4), gst(s, rs), (j0 + lane) * 4);
-    }
+    if (wv < 4) lds_load4(rsrc(p.grad + t * p.ld, nv * 4), gst(s) + wv * 256, (j0 + 64 * wv + lane) * 4);
+    else if (wv == 4) lds_load4(rsrc(p.w + t * kHeads, kHeads * 4), wst(s), lane * 4);
+    else lds_load4(rsrc(p.w, 0), dst_(s), lane * 4);
   };
-  constexpr int kLoadsPerQuery = 9;
+  constexpr int kLoadsPerQuery = 3;
 
   // transposed-read offsets of the Q^T operand of dk^T += Q^T . G'': rows (heads) 4*hf + jr
   // (+8), columns (dims) 32*mb + 16*(G&1) + 4*r .. +3
@@ -420,18 +421,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dk_kernel(BwdParams p) {
 
   if (iters > 0) {
     load_query(0, 0);
+    if (iters > 1) load_query(1, 1);
+    if (iters > 1) __builtin_amdgcn_s_waitcnt(kWaitVm | kLoadsPerQuery);
+    else __builtin_amdgcn_s_waitcnt(kWaitVm);
+    asm volatile("s_barrier" ::: "memory");
     for (int it = 0; it < iters; ++it) {
-      const int cur = it & 1;
-      if (it + 1 < iters) {
-        load_query(cur ^ 1, it + 1);
-        __builtin_amdgcn_s_waitcnt(kWaitVm | kLoadsPerQuery);
-      } else {
-        __builtin_amdgcn_s_waitcnt(kWaitVm);
-      }
-      asm volatile("s_barrier" ::: "memory");
-      const unsigned char* const qb = qst(cur, rs);
-      const float* const wb = reinterpret_cast<const float*>(wst(cur, rs));
-      const float gk = reinterpret_cast<const float*>(gst(cur, rs))[32 * kh + n];
+      if (it + 2 < iters) load_query((it + 2) % kStages, it + 2);
+      const int cur = it % kStages;
+      const unsigned char* const qb = qst(cur);
+      const float* const wb = reinterpret_cast<const float*>(wst(cur));
+      const float gk = reinterpret_cast<const float*>(gst(cur))[32 * wv + n];
 
       // S: row block rb = heads 32*rb + (accumulator rows), column = this lane's key
       f32x16 s0 = f32x16{}, s1 = f32x16{};
@@ -466,59 +465,68 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dk_kernel(BwdParams p) {
           dka[mb] = mfma(qa, gb[st], dka[mb]);
         }
       }
+      if (it + 2 < iters) __builtin_amdgcn_s_waitcnt(kWaitVm | kLoadsPerQuery);
+      else __builtin_amdgcn_s_waitcnt(kWaitVm);
       asm volatile("s_barrier" ::: "memory");
     }
   }
 
-  // Streams' sums through LDS: wave (rs, kh) stores register v = 16*mb + i of lane l at
-  // float index ((rs * 2 + kh) * 64 + v) * 64 + l.  Register i of dka[mb] holds dim
-  // 32*mb + 8*(i/4) + 4*hf + i%4 of key 32*kh + n.
+  // The unit's sums leave through LDS so that rows are written with 16-byte stores: wave wv
+  // puts register i of dka[mb] (dim 32*mb + 8*(i/4) + 4*hf + i%4 of key 32*wv + n) at
+  // row n, column dim of its own 32-row region.
   __syncthreads();
-  float* const red = reinterpret_cast<float*>(smem);
+  float* const ob = reinterpret_cast<float*>(smem) + wv * 32 * kDkOutStride;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) red[((wv * 64) + 16 * mb + i) * 64 + lane] = dka[mb][i];
+    for (int i = 0; i < 16; ++i)
+      ob[n * kDkOutStride + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3)] = dka[mb][i];
   __syncthreads();
-  // thread -> (key of the tile, 4 consecutive dims): 64 keys x 32 groups, 4 per thread
-  const int nkeys = min(kBwdKeyTile, lk_all - j0);
-  float* const out = p.part + ((int64_t)part * p.Tkv + ck + j0) * kDim;
+  const int nkeys = min(32, lk_all - j0 - 32 * wv);
+  float* const out = (parts == 1 ? p.dk : p.part + (int64_t)part * p.Tkv * kDim) +
+                     ((int64_t)ck + j0 + 32 * wv) * kDim;
 #pragma unroll
-  for (int rep = 0; rep < 4; ++rep) {
-    const int e = rep * kBwdThreads + tid;
-    const int key = e >> 5, dg = e & 31;       // dims 4*dg .. 4*dg+3
-    const int d0 = 4 * dg;
-    const int mb = d0 >> 5, g4 = (d0 >> 3) & 3, h2 = (d0 >> 2) & 1;
-    const int khk = key >> 5, l = (key & 31) + 32 * h2;
-    f32x4 v;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int reg = 16 * mb + 4 * g4 + c;
-      float x[kDkStreams];
-#pragma unroll
-      for (int r = 0; r < kDkStreams; ++r) x[r] = red[(((r * 2 + khk) * 64) + reg) * 64 + l];
-      v[c] = (x[0] + x[1]) + (x[2] + x[3]);
-    }
-    if (key < nkeys) *reinterpret_cast<f32x4*>(out + (int64_t)key * kDim + d0) = v;
+  for (int rep = 0; rep < 16; ++rep) {
+    const int e = rep * 64 + lane;
+    const int key = e >> 5, c4 = e & 31;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(ob + key * kDkOutStride + 4 * c4);
+    if (key < nkeys) *reinterpret_cast<f32x4*>(out + (int64_t)key * kDim + 4 * c4) = v;
   }
 }
 
-// dk = (P0 + P1) + (P2 + P3), four floats per thread, grid-stride.
+// dk = the P partials added in a fixed pairwise tree, four floats per thread, grid-stride.
+template <int P>
 __global__ __launch_bounds__(256) void bwd_dk_reduce_kernel(const float* __restrict__ part, float* __restrict__ dk,
-                                                            int64_t n4, int64_t stride, const uint32_t* ctrl) {
+                                                            int64_t n4, const uint32_t* ctrl) {
   if (ctrl[kCtrlStatus] & kStatusBadSegments) return;
-  const f32x4* P = reinterpret_cast<const f32x4*>(part);
+  const f32x4* src = reinterpret_cast<const f32x4*>(part);
   f32x4* out = reinterpret_cast<f32x4*>(dk);
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
-    const f32x4 a = P[i], b = P[i + stride], c = P[i + 2 * stride], d = P[i + 3 * stride];
-    out[i] = (a + b) + (c + d);
+    f32x4 v[P];
+#pragma unroll
+    for (int r = 0; r < P; ++r) v[r] = src[i + r * n4];
+#pragma unroll
+    for (int w = 1; w < P; w *= 2)
+#pragma unroll
+      for (int r = 0; r < P; r += 2 * w) v[r] = v[r] + v[r + w];
+    out[i] = v[0];
   }
 }
 
 }  // namespace
 
-size_t bwd_dq_smem_bytes() { return 2 * kDqStageBytes + kScratchInts * 4; }
-size_t bwd_dk_smem_bytes() { return 2 * kDkStageBytes + kScratchInts * 4; }
+size_t bwd_dq_smem_bytes() { return kStages * kDqStageBytes + kScratchInts * 4; }
+size_t bwd_dk_smem_bytes() {
+  const size_t area = kStages * kDkStageBytes > kDkOutBytes ? kStages * kDkStageBytes : kDkOutBytes;
+  return area + kScratchInts * 4;
+}
+
+int bwd_dk_parts(int64_t total_k) {
+  const int64_t blocks = (total_k + kDkKeys - 1) / kDkKeys;
+  int P = 1;
+  while (P < kDkMaxParts && blocks * P < kDkTargetUnits) P *= 2;
+  return P;
+}
 
 hipError_t bwd_prepare() {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_dq_kernel),
@@ -543,12 +551,20 @@ hipError_t launch_backward(const BwdParams& p, int dq_grid, int dk_grid, int cus
     hipLaunchKernelGGL(bwd_dk_kernel, dim3(dk_grid), dim3(kBwdThreads), bwd_dk_smem_bytes(), s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t n4 = (int64_t)p.Tkv * (kDim / 4);
-    const int64_t blocks = (n4 + 255) / 256;
-    const int grid = (int)(blocks < (int64_t)cus * 8 ? blocks : (int64_t)cus * 8);
-    hipLaunchKernelGGL(bwd_dk_reduce_kernel, dim3(grid), dim3(256), 0, s, p.part, p.dk, n4, n4, p.ctrl);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (p.dk_parts > 1) {
+      const int64_t n4 = (int64_t)p.Tkv * (kDim / 4);
+      const int64_t blocks = (n4 + 255) / 256;
+      const int grid = (int)(blocks < (int64_t)cus * 8 ? blocks : (int64_t)cus * 8);
+      switch (p.dk_parts) {
+        case 2: hipLaunchKernelGGL(bwd_dk_reduce_kernel<2>, dim3(grid), dim3(256), 0, s, p.part, p.dk, n4, p.ctrl); break;
+        case 4: hipLaunchKernelGGL(bwd_dk_reduce_kernel<4>, dim3(grid), dim3(256), 0, s, p.part, p.dk, n4, p.ctrl); break;
+        case 8: hipLaunchKernelGGL(bwd_dk_reduce_kernel<8>, dim3(grid), dim3(256), 0, s, p.part, p.dk, n4, p.ctrl); break;
+        case 16: hipLaunchKernelGGL(bwd_dk_reduce_kernel<16>, dim3(grid), dim3(256), 0, s, p.part, p.dk, n4, p.ctrl); break;
+        default: return hipErrorInvalidValue;
+      }
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }

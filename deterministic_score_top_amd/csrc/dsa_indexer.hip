@@ -320,7 +320,8 @@ int dsa_indexer_profiler_read(dsa_indexer_profiler* prof, double* score_ms, doub
 
 size_t dsa_indexer_backward_workspace_size(const dsa_indexer_shape* shape) {
   if (check_shape(shape) != DSA_OK) return 0;
-  return (size_t)dsa::kCtrlBytes + (size_t)dsa::kDkParts * (size_t)shape->total_k * dsa::kDim * 4u;
+  const int parts = dsa::bwd_dk_parts(shape->total_k);
+  return (size_t)dsa::kCtrlBytes + (parts > 1 ? (size_t)parts * (size_t)shape->total_k * dsa::kDim * 4u : 0u);
 }
 
 int dsa_indexer_backward_ex(const dsa_indexer_shape* shape, const void* q, const void* k,
@@ -361,9 +362,10 @@ int dsa_indexer_backward_ex(const dsa_indexer_shape* shape, const void* q, const
   p.T = shape->total_q;
   p.Tkv = shape->total_k;
   p.Lmax = (int32_t)lmax_of(shape);
+  p.dk_parts = dsa::bwd_dk_parts(shape->total_k);
   // unit counts are at most these bounds; blocks past the last unit leave at once
   const int64_t dq_grid = has_q ? (int64_t)(shape->total_q + dsa::kDqQueries - 1) / dsa::kDqQueries + shape->num_segments : 0;
-  const int64_t dk_grid = has_k ? ((int64_t)(shape->total_k + dsa::kBwdKeyTile - 1) / dsa::kBwdKeyTile + shape->num_segments) * dsa::kDkParts : 0;
+  const int64_t dk_grid = has_k ? ((int64_t)(shape->total_k + dsa::kDkKeys - 1) / dsa::kDkKeys + shape->num_segments) * p.dk_parts : 0;
   if (dq_grid > INT32_MAX || dk_grid > INT32_MAX) return DSA_ERR_SHAPE;
 
   hipEvent_t* ev = profiler ? &profiler->ev[3 * profiler->used] : nullptr;

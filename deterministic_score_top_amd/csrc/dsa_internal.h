@@ -66,8 +66,9 @@ struct SelectParams {
 constexpr int kBwdThreads = 512;
 constexpr int kBwdKeyTile = 64;  // keys per LDS tile
 constexpr int kDqQueries = 4;    // queries per dq unit (two waves per query, 32 heads each)
-constexpr int kDkStreams = 4;    // query streams per dk unit
-constexpr int kDkParts = 4;      // query parts per key tile; dk = fixed tree over the parts
+constexpr int kDkKeys = 256;     // keys per dk unit (32 per wave)
+constexpr int kDkMaxParts = 16;  // query parts per key block; dk = fixed tree over the parts
+constexpr int kDkTargetUnits = 512;
 
 struct BwdParams {
   const uint16_t* q;  // bf16 [T, H, D]
@@ -81,12 +82,15 @@ struct BwdParams {
   float* dq;    // fp32 [T, H, D]
   float* dk;    // fp32 [Tkv, D]
   float* dw;    // fp32 [T, H]
-  float* part;  // fp32 [kDkParts, Tkv, D] partial key gradients
+  float* part;  // fp32 [dk_parts, Tkv, D] partial key gradients (unused when dk_parts == 1)
   uint32_t* ctrl;
   int32_t B, T, Tkv, Lmax;
+  int32_t dk_parts;  // 1, 2, 4, 8 or 16, from bwd_dk_parts(Tkv)
 };
 
 size_t bwd_dq_smem_bytes();
+// Query parts per dk key block: a function of the number of keys only (about 512 units).
+int bwd_dk_parts(int64_t total_k);
 size_t bwd_dk_smem_bytes();
 hipError_t bwd_prepare();
 // `between` (may be null) is recorded after the dq/dw kernel.

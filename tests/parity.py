@@ -49,3 +49,26 @@ def check_rows(gpu_ids, gpu_scores, rows, oracle_ids, oracle_scores, detail, top
         except AssertionError as e:
             bad.append((t, str(e)))
     assert not bad, f"{len(bad)} bad rows, first: {bad[:3]}"
+
+
+def backward_row_bounds(q64, k64, w64, g, t, first, n):
+    """Error bounds of the GPU backward for query t's row (FP64 arrays, g = the row's n upstream
+    gradients): (dq [H, D], dw [H], dk terms [n, D] before the accumulation factor, dk mask-flip
+    terms [n, D]).
+
+    The GPU rounds the gradient factor of each product to BF16 (relative error <= 2^-8), sums
+    m terms in FP32 (<= m * 2^-24 of the sum of |terms|), and computes S in FP32 from exact
+    BF16 products (|error| <= 2^-17 * sum|q k|); where |S| is within 2^-16 * sum|q k| of zero
+    the ReLU mask may differ, so those terms enter the bound whole.
+    """
+    U = 2.0 ** -24
+    K = k64[first:first + n]
+    ag = np.abs(g)
+    aK, aq, aw = np.abs(K), np.abs(q64[t]), np.abs(w64[t])
+    S = q64[t] @ K.T
+    eps = 2.0 ** -16 * (aq @ aK.T)
+    amb = np.abs(S) <= eps
+    f = 2.0 ** -8 + (n + 10) * U
+    bq = aw[:, None] * (f * (ag @ aK)[None, :] + (amb * ag[None, :]) @ aK)
+    bw = eps @ ag + (n + 10) * U * (np.abs(S) @ ag)
+    return bq, bw, ag[:, None] * (aw @ aq)[None, :], ag[:, None] * ((amb * aw[:, None]).T @ aq)

@@ -122,7 +122,10 @@ def test_backward_argument_errors():
     L = ix.lib()
     V = ctypes.c_void_p
     s = ix.make_shape(16, 64, 1, 64)
-    assert ix.backward_workspace_size(16, 64, 1) == 256 + 4 * 64 * 128 * 4
+    # 64 keys: one 256-key block, 16 query parts -> 16 partials per key
+    assert ix.backward_workspace_size(16, 64, 1) == 256 + 16 * 64 * 128 * 4
+    # 175 428 keys: 686 key blocks fill the GPU alone, no partials
+    assert ix.backward_workspace_size(16, 175428, 1) == 256
     q, k, w, cq, ck, _, g, dq, ws = GOOD
     dk, dw = 0x90000, 0xA0000
 

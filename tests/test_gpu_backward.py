@@ -19,6 +19,7 @@ import torch
 from deterministic_score_top_amd import indexer as ix
 from deterministic_score_top_amd import workloads as W
 from oracle import dsa_oracle as O
+from tests.parity import backward_row_bounds as _row_bounds
 
 pytestmark = pytest.mark.gpu
 
@@ -42,21 +43,6 @@ def _gpu(wl, grad, **kw):
                              grad.to(d), offs, max_seqlen_k=wl.max_seqlen_k, **kw)
     torch.cuda.synchronize()
     return dq.cpu().numpy(), dk.cpu().numpy(), dw.cpu().numpy()
-
-
-def _row_bounds(q64, k64, w64, g, t, first, n):
-    """Bounds for query t's row: (dq [H, D], dw [H], dk terms [n, D] before the count factor,
-    dk mask-flip terms [n, D])."""
-    K = k64[first:first + n]
-    ag = np.abs(g)
-    aK, aq, aw = np.abs(K), np.abs(q64[t]), np.abs(w64[t])
-    S = q64[t] @ K.T
-    eps = 2.0 ** -16 * (aq @ aK.T)
-    amb = np.abs(S) <= eps
-    f = 2.0 ** -8 + (n + 10) * U
-    bq = aw[:, None] * (f * (ag @ aK)[None, :] + (amb * ag[None, :]) @ aK)
-    bw = eps @ ag + (n + 10) * U * (np.abs(S) @ ag)
-    return bq, bw, ag[:, None] * (aw @ aq)[None, :], ag[:, None] * ((amb * aw[:, None]).T @ aq)
 
 
 def _bounds(wl, grad):
@@ -291,3 +277,12 @@ def test_causal_n8192_sampled_rows_and_keys():
             flips += b[0]
         fk = 2.0 ** -8 + (64 * (wl.T - s) + 10) * U
         assert np.all(np.abs(dk[s] - acc) <= fk * scale + flips), s
+
+
+def test_exact_integer_many_keys_direct_dk():
+    # 140 000 keys: enough 256-key blocks that the dk kernel writes dk itself (no partials)
+    lens = [35000, 35000, 35000, 35000]
+    wl = W.integer_valued([8, 5, 0, 12], lens, [34992, 20000, 0, 34990], topk=8, seed=45, qk_range=2, w_den=8)
+    assert ix.backward_workspace_size(wl.T, wl.Tkv, wl.B, wl.max_seqlen_k) == 256
+    grad = W.draw_grad(wl.T, _ld(wl), seed=45, integer=True)
+    _check_exact(_gpu(wl, grad), O.backward_workload(wl, grad))
