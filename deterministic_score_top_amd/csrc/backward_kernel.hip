@@ -105,6 +105,10 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int jj) {
   return __builtin_convertvector(v, bf16x8);
 }
 
+// sched_group_barrier instruction classes
+constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100;
+#define DSA_SGB(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
 }
@@ -115,9 +119,15 @@ __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, unsigned cha
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 4, voff, 0, 0, 0);
 }
 
-// Byte offset, inside a 64-row x 256-byte LDS tile, of 16-byte chunk `chunk` of row `row`
-// (chunks XOR-swizzled by the row's low 4 bits).
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 15)) << 4); }
+// 16-byte chunk swizzle of a 64-row x 256-byte LDS tile: the chunk index is XORed with the
+// row's low 4 bits rotated by two (bits 0-1 to 2-3, bits 2-3 to 0-1).  It is a bijection on
+// any 16 consecutive rows, so a 16-byte read of one chunk from 16 rows hits 16 different
+// chunk positions (no bank conflict), and the 4 consecutive rows of a transposed read
+// (row & 3 = 0..3) move its 4 adjacent chunks into 4 different 64-byte groups.  (Plain
+// row & 15 leaves those 4 rows in one group: a 4-way conflict on every transposed read.)
+__device__ __forceinline__ int swzbits(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+// Byte offset of 16-byte chunk `chunk` of row `row`.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ swzbits(row)) << 4); }
 
 // Validates the segment tables (every thread of the block gets the flags): bit 0 = bad tables,
 // bit 1 = a segment longer than Lmax.  Block 0 records them in the status word.
@@ -230,7 +240,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p) {
     for (int r = 0; r < 2; ++r) {
       const int id = r * kWavesB + wv;
       const int row = 4 * id + (lane >> 4), pos = lane & 15;
-      lds_load16(krs, dst + id * 1024, (kt * kBwdKeyTile + row) * kRowBytes + ((pos ^ (row & 15)) << 4));
+      lds_load16(krs, dst + id * 1024, (kt * kBwdKeyTile + row) * kRowBytes + ((pos ^ swzbits(row)) << 4));
     }
     lds_load4(grs, dst + kTileBytes + wv * 256, (kt * kBwdKeyTile + lane) * 4);
   };
@@ -250,10 +260,82 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p) {
     }
   }
 
+  // per-lane offsets of the row-major K reads: row n, chunk 2*j + hf (row 32 + n is 8 KiB on)
+  int nat[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) nat[j] = swz(n, 2 * j + hf);
+
   f32x16 dqa[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) dqa[nb] = f32x16{};
   float dwa = 0.f;
+
+  // Epilogue of one S^T row block (16 keys of this lane's head in registers): G' = g where
+  // S > 0, else 0; dw += G' * S (equal to g * max(S, 0) bit for bit); G' packed to BF16 as
+  // the A operand of two K steps.  Key of register i: 32*rb + 8*(i/4) + 4*hf + i%4.
+  auto epilogue = [&](f32x16& sv, const float* gb, int rb, bf16x8& lo, bf16x8& hi) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(gb + 32 * rb + 8 * g4 + 4 * hf);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float e = sv[4 * g4 + c];
+        const float gp = pass_pos(e, gv[c]);
+        dwa = __builtin_fmaf(gp, e, dwa);
+        sv[4 * g4 + c] = gp;
+      }
+    }
+    lo = pack8(sv, 0);
+    hi = pack8(sv, 1);
+  };
+
+  // One key tile from the LDS stage `kb` (a constant offset after inlining).  Phases: S^T rows
+  // 0..31; rows 32..63 with the epilogue of rows 0..31 between the MFMAs; dq K steps 0, 1 with
+  // the epilogue of rows 32..63; dq K steps 2, 3.
+  auto tile = [&](const unsigned char* kb) {
+    const float* const gb = reinterpret_cast<const float*>(kb + kTileBytes + wv * 256);
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s0 = mfma(lds_b128(kb + nat[j]), qf[j], s0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s1 = mfma(lds_b128(kb + nat[j] + 32 * kRowBytes), qf[j], s1);
+    bf16x8 ga[4];
+    epilogue(s0, gb, 0, ga[0], ga[1]);
+    DSA_SGB(kSgDsRead, 8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      DSA_SGB(kSgMfma, 1);
+      DSA_SGB(kSgValu, 7);
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        dqa[nb] = mfma(ga[st], lds_tr_pair(kb + st * 16 * kRowBytes + trk1[nb], kb + st * 16 * kRowBytes + trk2[nb]),
+                       dqa[nb]);
+    epilogue(s1, gb, 1, ga[2], ga[3]);
+    DSA_SGB(kSgDsRead, 16);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      DSA_SGB(kSgMfma, 1);
+      DSA_SGB(kSgValu, 7);
+    }
+#pragma unroll
+    for (int st = 2; st < 4; ++st)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        dqa[nb] = mfma(ga[st], lds_tr_pair(kb + st * 16 * kRowBytes + trk1[nb], kb + st * 16 * kRowBytes + trk2[nb]),
+                       dqa[nb]);
+  };
+  // tile kt from stage c: first the load of tile kt + 2 into the stage every wave finished
+  // reading before the last barrier, then the tile, then wait for tile kt + 1 and meet
+  auto step = [&](int c, int kt) {
+    if (kt + 2 < ntk) load_tile((c + 2) % kStages, kt + 2);
+    tile(stage(c));
+    if (kt + 2 < ntk) __builtin_amdgcn_s_waitcnt(kWaitVm | kLoadsPerTile);
+    else __builtin_amdgcn_s_waitcnt(kWaitVm);
+    asm volatile("s_barrier" ::: "memory");
+  };
 
   if (ntk > 0) {
     load_tile(0, 0);
@@ -261,52 +343,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p) {
     if (ntk > 1) __builtin_amdgcn_s_waitcnt(kWaitVm | kLoadsPerTile);
     else __builtin_amdgcn_s_waitcnt(kWaitVm);
     asm volatile("s_barrier" ::: "memory");
-    for (int kt = 0; kt < ntk; ++kt) {
-      // tile kt + 2 goes to the buffer every wave finished reading before the last barrier
-      if (kt + 2 < ntk) load_tile((kt + 2) % kStages, kt + 2);
-      const unsigned char* const kb = stage(kt % kStages);
-      const float* const gb = reinterpret_cast<const float*>(kb + kTileBytes + wv * 256);
-
-      // S^T: row block rb = keys 32*rb + (accumulator rows), column = this lane's head
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bf16x8 a0 = lds_b128(kb + swz(n, 2 * j + hf));
-        const bf16x8 a1 = lds_b128(kb + swz(32 + n, 2 * j + hf));
-        s0 = mfma(a0, qf[j], s0);
-        s1 = mfma(a1, qf[j], s1);
-      }
-      // epilogue: key of accumulator register i in row block rb = 32*rb + 8*(i/4) + 4*hf + i%4
-      bf16x8 ga[4];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        f32x16& sv = rb ? s1 : s0;
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 gv = *reinterpret_cast<const f32x4*>(gb + 32 * rb + 8 * g4 + 4 * hf);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float e = sv[4 * g4 + c];
-            dwa = __builtin_fmaf(gv[c], relu_bits(e), dwa);
-            sv[4 * g4 + c] = pass_pos(e, gv[c]);
-          }
-        }
-        ga[2 * rb] = pack8(sv, 0);
-        ga[2 * rb + 1] = pack8(sv, 1);
-      }
-      // dq[h, d] += sum over the tile's keys of G'[h, key] * K[key, d]
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const bf16x8 bk = lds_tr_pair(kb + st * 16 * kRowBytes + trk1[nb], kb + st * 16 * kRowBytes + trk2[nb]);
-          dqa[nb] = mfma(ga[st], bk, dqa[nb]);
-        }
-      }
-      // tile kt + 1 must have landed (only tile kt + 2's loads may still be in flight)
-      if (kt + 2 < ntk) __builtin_amdgcn_s_waitcnt(kWaitVm | kLoadsPerTile);
-      else __builtin_amdgcn_s_waitcnt(kWaitVm);
-      asm volatile("s_barrier" ::: "memory");
+    for (int kt = 0; kt < ntk; kt += kStages) {
+      step(0, kt);
+      if (kt + 1 < ntk) step(1, kt + 1);
+      if (kt + 2 < ntk) step(2, kt + 2);
     }
   }
 
@@ -393,7 +433,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dk_kernel(BwdParams p) {
     for (int r = 0; r < 2; ++r) {
       const int id = r * kWavesB + wv;
       const int row = 4 * id + (lane >> 4), pos = lane & 15;
-      lds_load16(qrs, qd + id * 1024, row * kRowBytes + ((pos ^ (row & 15)) << 4));
+      lds_load16(qrs, qd + id * 1024, row * kRowBytes + ((pos ^ swzbits(row)) << 4));
     }
     if (wv < 4) lds_load4(rsrc(p.grad + t * p.ld, nv * 4), gst(s) + wv * 256, (j0 + 64 * wv + lane) * 4);
     else if (wv == 4) lds_load4(rsrc(p.w + t * kHeads, kHeads * 4), wst(s), lane * 4);
@@ -415,9 +455,71 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dk_kernel(BwdParams p) {
     }
   }
 
+  int nat[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) nat[j] = swz(n, 2 * j + hf);
+
   f32x16 dka[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) dka[mb] = f32x16{};
+
+  // G'' = w[h] * g[key] where S > 0, packed to BF16 as the B operand of two K steps; head of
+  // register i in row block rb: 32*rb + 8*(i/4) + 4*hf + i%4
+  auto epilogue = [&](f32x16& sv, const float* wb, float gk, int rb, bf16x8& lo, bf16x8& hi) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 wv4 = *reinterpret_cast<const f32x4*>(wb + 32 * rb + 8 * g4 + 4 * hf);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sv[4 * g4 + c] = pass_pos(sv[4 * g4 + c], wv4[c] * gk);
+    }
+    lo = pack8(sv, 0);
+    hi = pack8(sv, 1);
+  };
+  // One query from the LDS stage `qb`: S rows (heads) 0..31; rows 32..63 with the epilogue of
+  // rows 0..31; dk K steps 0, 1 with the epilogue of rows 32..63; dk K steps 2, 3.
+  auto query = [&](const unsigned char* qb) {
+    const float* const wb = reinterpret_cast<const float*>(qb + kTileBytes + kDkKeys * 4);
+    const float gk = reinterpret_cast<const float*>(qb + kTileBytes)[32 * wv + n];
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s0 = mfma(lds_b128(qb + nat[j]), kf[j], s0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s1 = mfma(lds_b128(qb + nat[j] + 32 * kRowBytes), kf[j], s1);
+    bf16x8 gb[4];
+    epilogue(s0, wb, gk, 0, gb[0], gb[1]);
+    DSA_SGB(kSgDsRead, 8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      DSA_SGB(kSgMfma, 1);
+      DSA_SGB(kSgValu, 7);
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        dka[mb] = mfma(lds_tr_pair(qb + st * 16 * kRowBytes + trq1[mb], qb + st * 16 * kRowBytes + trq2[mb]), gb[st],
+                       dka[mb]);
+    epilogue(s1, wb, gk, 1, gb[2], gb[3]);
+    DSA_SGB(kSgDsRead, 16);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      DSA_SGB(kSgMfma, 1);
+      DSA_SGB(kSgValu, 7);
+    }
+#pragma unroll
+    for (int st = 2; st < 4; ++st)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        dka[mb] = mfma(lds_tr_pair(qb + st * 16 * kRowBytes + trq1[mb], qb + st * 16 * kRowBytes + trq2[mb]), gb[st],
+                       dka[mb]);
+  };
+  auto step = [&](int c, int it) {
+    if (it + 2 < iters) load_query((c + 2) % kStages, it + 2);
+    query(qst(c));
+    if (it + 2 < iters) __builtin_amdgcn_s_waitcnt(kWaitVm | kLoadsPerQuery);
+    else __builtin_amdgcn_s_waitcnt(kWaitVm);
+    asm volatile("s_barrier" ::: "memory");
+  };
 
   if (iters > 0) {
     load_query(0, 0);
@@ -425,49 +527,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dk_kernel(BwdParams p) {
     if (iters > 1) __builtin_amdgcn_s_waitcnt(kWaitVm | kLoadsPerQuery);
     else __builtin_amdgcn_s_waitcnt(kWaitVm);
     asm volatile("s_barrier" ::: "memory");
-    for (int it = 0; it < iters; ++it) {
-      if (it + 2 < iters) load_query((it + 2) % kStages, it + 2);
-      const int cur = it % kStages;
-      const unsigned char* const qb = qst(cur);
-      const float* const wb = reinterpret_cast<const float*>(wst(cur));
-      const float gk = reinterpret_cast<const float*>(gst(cur))[32 * wv + n];
-
-      // S: row block rb = heads 32*rb + (accumulator rows), column = this lane's key
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bf16x8 a0 = lds_b128(qb + swz(n, 2 * j + hf));
-        const bf16x8 a1 = lds_b128(qb + swz(32 + n, 2 * j + hf));
-        s0 = mfma(a0, kf[j], s0);
-        s1 = mfma(a1, kf[j], s1);
-      }
-      // G'' = w[h] * g[key] where S > 0; head of register i in row block rb:
-      // 32*rb + 8*(i/4) + 4*hf + i%4
-      bf16x8 gb[4];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        f32x16& sv = rb ? s1 : s0;
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 wv4 = *reinterpret_cast<const f32x4*>(wb + 32 * rb + 8 * g4 + 4 * hf);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) sv[4 * g4 + c] = pass_pos(sv[4 * g4 + c], wv4[c] * gk);
-        }
-        gb[2 * rb] = pack8(sv, 0);
-        gb[2 * rb + 1] = pack8(sv, 1);
-      }
-      // dk^T[d, key] += sum over heads of Q^T[d, h] * G''[h, key]
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          const bf16x8 qa = lds_tr_pair(qb + st * 16 * kRowBytes + trq1[mb], qb + st * 16 * kRowBytes + trq2[mb]);
-          dka[mb] = mfma(qa, gb[st], dka[mb]);
-        }
-      }
-      if (it + 2 < iters) __builtin_amdgcn_s_waitcnt(kWaitVm | kLoadsPerQuery);
-      else __builtin_amdgcn_s_waitcnt(kWaitVm);
-      asm volatile("s_barrier" ::: "memory");
+    for (int it = 0; it < iters; it += kStages) {
+      step(0, it);
+      if (it + 1 < iters) step(1, it + 1);
+      if (it + 2 < iters) step(2, it + 2);
     }
   }
 
