@@ -11,7 +11,8 @@
 // ReLU at exactly 0 is 0.
 //
 // Three kernels, no atomics on any gradient, every sum in a fixed order:
-//   * dq/dw kernel, query-major: a unit is 4 consecutive queries of one segment; wave w takes
+//   * dq/dw kernel, query-major: a unit is 4 consecutive queries of one segment (and, when
+//     there are few queries, one of P even shares of their key tiles); wave w takes
 //     query w/2 and heads 32*(w%2) .. +31.  Key tiles land in LDS two ahead (three buffers,
 //     one barrier per tile).  Per 64-key tile it recomputes S^T = K . Q^T
 //     (v_mfma_f32_32x32x16_bf16, K tile from LDS, Q in VGPRs), forms dw partials in FP32 and
@@ -26,8 +27,10 @@
 //     A query's 16 KiB q block thus serves 256 keys per load.  P (1, 2, 4, 8 or 16) depends
 //     only on the number of keys: enough parts for about 512 units.  With P = 1 the unit
 //     writes dk itself; otherwise it writes an FP32 partial.
-//   * reduce kernel (P > 1): dk = the P partials added in a fixed pairwise tree
-//     ((P0 + P1) + (P2 + P3)) + ...
+//   * reduce kernels (P > 1): dk = the P partials added in a fixed pairwise tree
+//     ((P0 + P1) + (P2 + P3)) + ...; likewise dq and dw when few query tiles leave room for
+//     splitting each tile's keys over P units (P from the number of queries only; w is applied
+//     after the tree).
 //
 // MFMA layout used throughout (32x32x16 BF16): operand lane l carries row/column l % 32 and
 // K elements 8 * (l / 32) .. +7; accumulator register i of lane l holds row
@@ -203,20 +206,25 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p) {
 
   if (table_flags(p, scratch) & 1) return;
   int idx = 0;
+  const int parts = p.dq_parts;
   const int b = locate_unit(p.B, blockIdx.x, [&](int s) -> uint32_t {
     const int lq = p.cu_q[s + 1] - p.cu_q[s];
-    return (uint32_t)ceil_div(lq, kDqQueries);
+    return (uint32_t)(ceil_div(lq, kDqQueries) * parts);
   }, scratch, &idx);
   if (b < 0) return;
 
   const int cq = p.cu_q[b], lq = p.cu_q[b + 1] - cq;
   const int ck = p.cu_k[b], lk = min(p.cu_k[b + 1] - ck, p.Lmax);
   const int64_t off = p.offs ? p.offs[b] : 0;
-  const int ti = ceil_div(lq, kDqQueries) - 1 - idx;   // most visible keys first
+  const int ti = ceil_div(lq, kDqQueries) - 1 - idx / parts;   // most visible keys first
+  const int part = idx % parts;
   const int tq0 = ti * kDqQueries;
   const int nq = min(kDqQueries, lq - tq0);
   const int nmax = clampi(off + tq0 + nq, 0, lk);
-  const int ntk = ceil_div(nmax, kBwdKeyTile);
+  // this unit's share of the tile's key tiles: [kt0, kt0 + ntk)
+  const int ntk_all = ceil_div(nmax, kBwdKeyTile);
+  const int kt0 = (int)((int64_t)part * ntk_all / parts);
+  const int ntk = (int)((int64_t)(part + 1) * ntk_all / parts) - kt0;
   const bool qvalid = qi < nq;
   const int64_t t = (int64_t)cq + tq0 + min(qi, nq - 1);
   const int nt = __builtin_amdgcn_readfirstlane(qvalid ? clampi(off + tq0 + qi + 1, 0, lk) : 0);
@@ -240,9 +248,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p) {
     for (int r = 0; r < 2; ++r) {
       const int id = r * kWavesB + wv;
       const int row = 4 * id + (lane >> 4), pos = lane & 15;
-      lds_load16(krs, dst + id * 1024, (kt * kBwdKeyTile + row) * kRowBytes + ((pos ^ swzbits(row)) << 4));
+      lds_load16(krs, dst + id * 1024, ((kt0 + kt) * kBwdKeyTile + row) * kRowBytes + ((pos ^ swzbits(row)) << 4));
     }
-    lds_load4(grs, dst + kTileBytes + wv * 256, (kt * kBwdKeyTile + lane) * 4);
+    lds_load4(grs, dst + kTileBytes + wv * 256, ((kt0 + kt) * kBwdKeyTile + lane) * 4);
   };
   constexpr int kLoadsPerTile = 3;
 
@@ -351,24 +359,27 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p) {
   }
 
   if (!qvalid) return;
-  // dq = w * accumulated sum; accumulator register i of dqa[nb]: head 32*hg + 8*(i/4) + 4*hf + i%4,
-  // dim 32*nb + n
+  // accumulator register i of dqa[nb]: head 32*hg + 8*(i/4) + 4*hf + i%4, dim 32*nb + n.  One
+  // part: dq = w * sum.  Several: the unscaled sum is this part's partial; the reduce kernel adds
+  // the parts in a fixed tree and then applies w.
+  const int64_t prow = (int64_t)part * p.T + t;
+  float* const dqrow = (parts == 1 ? p.dq + t * (kHeads * kDim) : p.part_q + prow * (kHeads * kDim)) +
+                       (32 * hg + 4 * hf) * kDim + n;
   const float* const wrow = p.w + t * kHeads + 32 * hg + 4 * hf;
-  float* const dqrow = p.dq + (t * kHeads + 32 * hg + 4 * hf) * kDim + n;
 #pragma unroll
   for (int g4 = 0; g4 < 4; ++g4) {
-    const f32x4 wv4 = *reinterpret_cast<const f32x4*>(wrow + 8 * g4);
+    const f32x4 wv4 = parts == 1 ? *reinterpret_cast<const f32x4*>(wrow + 8 * g4) : f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
-        dqrow[(8 * g4 + c) * kDim + 32 * nb] = wv4[c] * dqa[nb][4 * g4 + c];
+        dqrow[(8 * g4 + c) * kDim + 32 * nb] = parts == 1 ? wv4[c] * dqa[nb][4 * g4 + c] : dqa[nb][4 * g4 + c];
     }
   }
   // dw: lanes n and n + 32 hold the same head's sums over disjoint keys
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(dwa), __float_as_uint(dwa), false, false);
   const float dwt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-  if (hf == 0) p.dw[t * kHeads + 32 * hg + n] = dwt;
+  if (hf == 0) (parts == 1 ? p.dw + t * kHeads : p.part_w + prow * kHeads)[32 * hg + n] = dwt;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -557,22 +568,50 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dk_kernel(BwdParams p) {
   }
 }
 
-// dk = the P partials added in a fixed pairwise tree, four floats per thread, grid-stride.
+// Sum of the P partials src[i + r * stride], r = 0 .. P-1, as the pairwise tree
+// ((r0 + r1) + (r2 + r3)) + ... (P a power of two).
+template <int P>
+struct Tree {
+  __device__ __forceinline__ static f32x4 sum(const f32x4* src, int64_t i, int64_t stride, int r0) {
+    return Tree<P / 2>::sum(src, i, stride, r0) + Tree<P / 2>::sum(src, i, stride, r0 + P / 2);
+  }
+};
+template <>
+struct Tree<1> {
+  __device__ __forceinline__ static f32x4 sum(const f32x4* src, int64_t i, int64_t stride, int r0) {
+    return src[i + r0 * stride];
+  }
+};
+
+// dk = the P partials added in the fixed pairwise tree, four floats per thread, grid-stride.
 template <int P>
 __global__ __launch_bounds__(256) void bwd_dk_reduce_kernel(const float* __restrict__ part, float* __restrict__ dk,
                                                             int64_t n4, const uint32_t* ctrl) {
   if (ctrl[kCtrlStatus] & kStatusBadSegments) return;
   const f32x4* src = reinterpret_cast<const f32x4*>(part);
   f32x4* out = reinterpret_cast<f32x4*>(dk);
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
-    f32x4 v[P];
-#pragma unroll
-    for (int r = 0; r < P; ++r) v[r] = src[i + r * n4];
-#pragma unroll
-    for (int w = 1; w < P; w *= 2)
-#pragma unroll
-      for (int r = 0; r < P; r += 2 * w) v[r] = v[r] + v[r + w];
-    out[i] = v[0];
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = Tree<P>::sum(src, i, n4, 0);
+}
+
+// dq = w * (the P partial sums added in the fixed pairwise tree); dw = the tree of its partials.
+template <int P>
+__global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const float* __restrict__ part_q,
+                                                            const float* __restrict__ part_w,
+                                                            const float* __restrict__ w, float* __restrict__ dq,
+                                                            float* __restrict__ dw, int64_t T, const uint32_t* ctrl) {
+  if (ctrl[kCtrlStatus] & kStatusBadSegments) return;
+  const int64_t nq4 = T * (kHeads * kDim / 4), nw4 = T * (kHeads / 4);
+  const f32x4* sq = reinterpret_cast<const f32x4*>(part_q);
+  const f32x4* sw = reinterpret_cast<const f32x4*>(part_w);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nq4 + nw4; i += (int64_t)gridDim.x * blockDim.x) {
+    if (i < nq4) {
+      const float wt = w[i / (kDim / 4)];   // row (t, h) of the f32x4 group
+      reinterpret_cast<f32x4*>(dq)[i] = wt * Tree<P>::sum(sq, i, nq4, 0);
+    } else {
+      const int64_t j = i - nq4;
+      reinterpret_cast<f32x4*>(dw)[j] = Tree<P>::sum(sw, j, nw4, 0);
+    }
   }
 }
 
@@ -587,7 +626,15 @@ size_t bwd_dk_smem_bytes() {
 int bwd_dk_parts(int64_t total_k) {
   const int64_t blocks = (total_k + kDkKeys - 1) / kDkKeys;
   int P = 1;
-  while (P < kDkMaxParts && blocks * P < kDkTargetUnits) P *= 2;
+  while (blocks > 0 && P < kBwdMaxParts && blocks * P < kBwdTargetUnits) P *= 2;
+  return P;
+}
+
+int bwd_dq_parts(int64_t total_q) {
+  const int64_t tiles = (total_q + kDqQueries - 1) / kDqQueries;
+  int P = 1;
+  // one unit per CU is enough here: splitting a tile's keys costs a pass over the partials
+  while (tiles > 0 && P < kBwdMaxParts && tiles * P < kBwdTargetUnits / 2) P *= 2;
   return P;
 }
 
@@ -605,6 +652,23 @@ hipError_t launch_backward(const BwdParams& p, int dq_grid, int dk_grid, int cus
     hipLaunchKernelGGL(bwd_dq_kernel, dim3(dq_grid), dim3(kBwdThreads), bwd_dq_smem_bytes(), s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (p.dq_parts > 1) {
+      const int64_t n4 = (int64_t)p.T * (kHeads * kDim / 4 + kHeads / 4);
+      const int64_t blocks = (n4 + 255) / 256;
+      const int grid = (int)(blocks < (int64_t)cus * 8 ? blocks : (int64_t)cus * 8);
+#define DSA_DQ_REDUCE(P)                                                                                      \
+  case P:                                                                                                     \
+    hipLaunchKernelGGL(bwd_dq_reduce_kernel<P>, dim3(grid), dim3(256), 0, s, p.part_q, p.part_w, p.w, p.dq, \
+                       p.dw, (int64_t)p.T, p.ctrl);                                                           \
+    break;
+      switch (p.dq_parts) {
+        DSA_DQ_REDUCE(2) DSA_DQ_REDUCE(4) DSA_DQ_REDUCE(8) DSA_DQ_REDUCE(16) DSA_DQ_REDUCE(32) DSA_DQ_REDUCE(64)
+        default: return hipErrorInvalidValue;
+      }
+#undef DSA_DQ_REDUCE
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   if (between) {
     hipError_t e = hipEventRecord(between, s);
@@ -618,13 +682,15 @@ hipError_t launch_backward(const BwdParams& p, int dq_grid, int dk_grid, int cus
       const int64_t n4 = (int64_t)p.Tkv * (kDim / 4);
       const int64_t blocks = (n4 + 255) / 256;
       const int grid = (int)(blocks < (int64_t)cus * 8 ? blocks : (int64_t)cus * 8);
+#define DSA_DK_REDUCE(P)                                                                         \
+  case P:                                                                                        \
+    hipLaunchKernelGGL(bwd_dk_reduce_kernel<P>, dim3(grid), dim3(256), 0, s, p.part, p.dk, n4, p.ctrl); \
+    break;
       switch (p.dk_parts) {
-        case 2: hipLaunchKernelGGL(bwd_dk_reduce_kernel<2>, dim3(grid), dim3(256), 0, s, p.part, p.dk, n4, p.ctrl); break;
-        case 4: hipLaunchKernelGGL(bwd_dk_reduce_kernel<4>, dim3(grid), dim3(256), 0, s, p.part, p.dk, n4, p.ctrl); break;
-        case 8: hipLaunchKernelGGL(bwd_dk_reduce_kernel<8>, dim3(grid), dim3(256), 0, s, p.part, p.dk, n4, p.ctrl); break;
-        case 16: hipLaunchKernelGGL(bwd_dk_reduce_kernel<16>, dim3(grid), dim3(256), 0, s, p.part, p.dk, n4, p.ctrl); break;
+        DSA_DK_REDUCE(2) DSA_DK_REDUCE(4) DSA_DK_REDUCE(8) DSA_DK_REDUCE(16) DSA_DK_REDUCE(32) DSA_DK_REDUCE(64)
         default: return hipErrorInvalidValue;
       }
+#undef DSA_DK_REDUCE
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

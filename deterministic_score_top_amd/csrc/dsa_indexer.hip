@@ -320,8 +320,11 @@ int dsa_indexer_profiler_read(dsa_indexer_profiler* prof, double* score_ms, doub
 
 size_t dsa_indexer_backward_workspace_size(const dsa_indexer_shape* shape) {
   if (check_shape(shape) != DSA_OK) return 0;
-  const int parts = dsa::bwd_dk_parts(shape->total_k);
-  return (size_t)dsa::kCtrlBytes + (parts > 1 ? (size_t)parts * (size_t)shape->total_k * dsa::kDim * 4u : 0u);
+  const int pk = dsa::bwd_dk_parts(shape->total_k), pq = dsa::bwd_dq_parts(shape->total_q);
+  size_t n = (size_t)dsa::kCtrlBytes;
+  if (pk > 1) n += (size_t)pk * (size_t)shape->total_k * dsa::kDim * 4u;
+  if (pq > 1) n += (size_t)pq * (size_t)shape->total_q * (dsa::kHeads * dsa::kDim + dsa::kHeads) * 4u;
+  return n;
 }
 
 int dsa_indexer_backward_ex(const dsa_indexer_shape* shape, const void* q, const void* k,
@@ -363,8 +366,17 @@ int dsa_indexer_backward_ex(const dsa_indexer_shape* shape, const void* q, const
   p.Tkv = shape->total_k;
   p.Lmax = (int32_t)lmax_of(shape);
   p.dk_parts = dsa::bwd_dk_parts(shape->total_k);
+  p.dq_parts = dsa::bwd_dq_parts(shape->total_q);
+  {
+    // workspace: control block | dk partials (dk_parts > 1) | dq partials, dw partials (dq_parts > 1)
+    float* cur = p.part + (p.dk_parts > 1 ? (int64_t)p.dk_parts * shape->total_k * dsa::kDim : 0);
+    p.part_q = cur;
+    cur += p.dq_parts > 1 ? (int64_t)p.dq_parts * shape->total_q * dsa::kHeads * dsa::kDim : 0;
+    p.part_w = cur;
+  }
   // unit counts are at most these bounds; blocks past the last unit leave at once
-  const int64_t dq_grid = has_q ? (int64_t)(shape->total_q + dsa::kDqQueries - 1) / dsa::kDqQueries + shape->num_segments : 0;
+  const int64_t dq_grid =
+      has_q ? ((int64_t)(shape->total_q + dsa::kDqQueries - 1) / dsa::kDqQueries + shape->num_segments) * p.dq_parts : 0;
   const int64_t dk_grid = has_k ? ((int64_t)(shape->total_k + dsa::kDkKeys - 1) / dsa::kDkKeys + shape->num_segments) * p.dk_parts : 0;
   if (dq_grid > INT32_MAX || dk_grid > INT32_MAX) return DSA_ERR_SHAPE;
 

@@ -67,8 +67,8 @@ constexpr int kBwdThreads = 512;
 constexpr int kBwdKeyTile = 64;  // keys per LDS tile
 constexpr int kDqQueries = 4;    // queries per dq unit (two waves per query, 32 heads each)
 constexpr int kDkKeys = 256;     // keys per dk unit (32 per wave)
-constexpr int kDkMaxParts = 16;  // query parts per key block; dk = fixed tree over the parts
-constexpr int kDkTargetUnits = 512;
+constexpr int kBwdMaxParts = 64;  // parts per key block (dk) or query tile (dq); fixed trees over them
+constexpr int kBwdTargetUnits = 512;
 
 struct BwdParams {
   const uint16_t* q;  // bf16 [T, H, D]
@@ -85,12 +85,17 @@ struct BwdParams {
   float* part;  // fp32 [dk_parts, Tkv, D] partial key gradients (unused when dk_parts == 1)
   uint32_t* ctrl;
   int32_t B, T, Tkv, Lmax;
-  int32_t dk_parts;  // 1, 2, 4, 8 or 16, from bwd_dk_parts(Tkv)
+  int32_t dk_parts;  // 1, 2, 4, .. 64, from bwd_dk_parts(Tkv)
+  int32_t dq_parts;  // 1, 2, 4, .. 64, from bwd_dq_parts(T)
+  float* part_q;     // fp32 [dq_parts, T, H, D] unscaled partial dq (dq_parts > 1)
+  float* part_w;     // fp32 [dq_parts, T, H] partial dw (dq_parts > 1)
 };
 
 size_t bwd_dq_smem_bytes();
 // Query parts per dk key block: a function of the number of keys only (about 512 units).
 int bwd_dk_parts(int64_t total_k);
+// Key-tile parts per dq query tile: a function of the number of queries only.
+int bwd_dq_parts(int64_t total_q);
 size_t bwd_dk_smem_bytes();
 hipError_t bwd_prepare();
 // `between` (may be null) is recorded after the dq/dw kernel.

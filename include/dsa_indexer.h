@@ -149,9 +149,10 @@ int dsa_indexer_scores(const dsa_indexer_shape* shape, const void* q, const void
  *   dq             fp32 [T, 64, 128], dk fp32 [Tkv, 128], dw fp32 [T, 64]: fully overwritten
  *                  (keys no query sees and queries that see no key get zeros)
  *   workspace      >= dsa_indexer_backward_workspace_size(shape) bytes, initialised once
- *                  (dsa_indexer_workspace_init); holds the status word and, when total_k is
- *                  small enough that key blocks alone cannot fill the GPU, P FP32 partial key
- *                  gradients per key (P = 2 .. 16, a function of total_k only)
+ *                  (dsa_indexer_workspace_init); holds the status word and, when total_k
+ *                  (total_q) is small enough that key blocks (query tiles) alone cannot fill
+ *                  the GPU, P FP32 partial key (query and weight) gradients per key (query),
+ *                  P = 2 .. 64 a function of total_k (total_q) only
  * Bit-reproducible: every sum has a fixed order that depends only on the segment tables.
  * Invalid device tables (DSA_STATUS_BAD_SEGMENTS) leave the outputs untouched; a segment
  * longer than max_seqlen_k is flagged (DSA_STATUS_SEQLEN_BOUND) and its keys past the bound

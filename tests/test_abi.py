@@ -122,10 +122,14 @@ def test_backward_argument_errors():
     L = ix.lib()
     V = ctypes.c_void_p
     s = ix.make_shape(16, 64, 1, 64)
-    # 64 keys: one 256-key block, 16 query parts -> 16 partials per key
-    assert ix.backward_workspace_size(16, 64, 1) == 256 + 16 * 64 * 128 * 4
-    # 175 428 keys: 686 key blocks fill the GPU alone, no partials
-    assert ix.backward_workspace_size(16, 175428, 1) == 256
+    # 16 queries: 4 query tiles, each split over 64 key parts (dq and dw partials); 64 keys: one
+    # 256-key block split over 64 query parts (dk partials)
+    dq_part = 64 * 16 * (64 * 128 + 64) * 4
+    assert ix.backward_workspace_size(16, 64, 1) == 256 + 64 * 64 * 128 * 4 + dq_part
+    # 175 428 keys: 686 key blocks fill the GPU alone, no dk partials
+    assert ix.backward_workspace_size(16, 175428, 1) == 256 + dq_part
+    # 8192 queries and keys: 2048 query tiles, 32 key blocks x 16 parts
+    assert ix.backward_workspace_size(8192, 8192, 1) == 256 + 16 * 8192 * 128 * 4
     q, k, w, cq, ck, _, g, dq, ws = GOOD
     dk, dw = 0x90000, 0xA0000
 

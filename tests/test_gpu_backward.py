@@ -283,6 +283,7 @@ def test_exact_integer_many_keys_direct_dk():
     # 140 000 keys: enough 256-key blocks that the dk kernel writes dk itself (no partials)
     lens = [35000, 35000, 35000, 35000]
     wl = W.integer_valued([8, 5, 0, 12], lens, [34992, 20000, 0, 34990], topk=8, seed=45, qk_range=2, w_den=8)
-    assert ix.backward_workspace_size(wl.T, wl.Tkv, wl.B, wl.max_seqlen_k) == 256
+    # no dk partials (the 25 queries do get 64 key parts each: dq and dw partials)
+    assert ix.backward_workspace_size(wl.T, wl.Tkv, wl.B, wl.max_seqlen_k) == 256 + 64 * wl.T * (64 * 128 + 64) * 4
     grad = W.draw_grad(wl.T, _ld(wl), seed=45, integer=True)
     _check_exact(_gpu(wl, grad), O.backward_workload(wl, grad))
