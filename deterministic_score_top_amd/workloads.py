@@ -212,6 +212,15 @@ def draw_grad(T: int, ld: int, seed: int = 0, integer: bool = False) -> torch.Te
     return torch.randn((T, ld), generator=g, dtype=torch.float32)
 
 
+def draw_attention(T: int, Tkv: int, H: int = 128, dqk: int = 576, seed: int = 0):
+    """Inputs of the sparse attention that consumes the selection: q bf16 [T, H, dqk] ~ N(0,1)
+    and the latent KV table bf16 [Tkv, dqk] ~ N(0,1)."""
+    g = _gen(seed + 104729)
+    q = torch.randn((T, H, dqk), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    kv = torch.randn((Tkv, dqk), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    return q, kv
+
+
 CONFIGS = {
     # name: (builder, description)
     "causal_n1024": lambda seed=0: single_causal(1024, 256, seed, "causal_n1024"),

@@ -50,6 +50,18 @@ with S[t, h, j] = q[t, h, :] . k[s, :].  The ReLU's derivative at exactly 0
 is taken as 0 (the usual convention; the pages are silent).  Keys no query
 sees get dk = 0, queries that see no key get dq = dw = 0.
 
+Consumer of the selection (flashinfer PR #4573, "feat(cake_sparse_mla): support SM100 and
+SM103", and its follow-up hardening the DeepSeek-V4 sparse-MLA decode path): for each query
+row the attention reads the row's selected key ids, never dereferences -1, gathers those
+rows of the shared latent KV table and attends over them; the value operand is served from
+the gathered key rows (MLA: the value is the first dv dims of the same row).  The pages
+print no formula; the oracle takes standard scaled-dot-product attention over the valid ids
+of row t, for every head h:
+        S[h, j] = scale * q[t, h, :] . kv[id_j, :]          (valid j: id_j >= 0)
+        o[t, h, :] = sum_j softmax_j(S[h, :]) * kv[id_j, :dv]
+        lse[t, h] = log sum_j exp(S[h, j])
+A row with no valid id has o = 0 and lse = -inf.
+
 Everything here is FP64: BF16 and FP32 inputs convert to FP64 exactly, the
 dot products use a library matmul, the head reduction a library
 matrix-vector product, and the selection a library lexicographic sort on
@@ -184,3 +196,32 @@ def backward_workload(wl, grad):
     g = grad.double().numpy() if hasattr(grad, "double") else np.asarray(grad, dtype=np.float64)
     offs = None if wl.q_pos_offsets is None else wl.q_pos_offsets.numpy()
     return backward_rows(q64, k64, w64, wl.cu_seqlens_q.numpy(), wl.cu_seqlens_k.numpy(), offs, g)
+
+
+def sparse_attention_row(q64_t: np.ndarray, kv64: np.ndarray, ids_row, scale: float, dv: int):
+    """o [H, dv] and lse [H] of one query row (q64_t [H, Dqk]) over its valid ids."""
+    ids_row = np.asarray(ids_row, dtype=np.int64)
+    valid = ids_row[ids_row >= 0]
+    H = q64_t.shape[0]
+    if valid.size == 0:
+        return np.zeros((H, dv)), np.full(H, NEG_INF)
+    K = kv64[valid]                                   # [m, Dqk] gathered rows
+    S = scale * (q64_t @ K.T)                         # [H, m]
+    mx = S.max(axis=1, keepdims=True)
+    E = np.exp(S - mx)
+    den = E.sum(axis=1, keepdims=True)
+    o = (E / den) @ K[:, :dv]
+    lse = (mx + np.log(den))[:, 0]
+    return o, lse
+
+
+def sparse_attention_rows(q64, kv64, ids, scale: float, dv: int, rows=None):
+    """o [R, H, dv], lse [R, H] for the given query rows (all if None); ids int [T, k], -1 = none."""
+    T, H = q64.shape[0], q64.shape[1]
+    rows = range(T) if rows is None else list(rows)
+    rows = list(rows)
+    o = np.zeros((len(rows), H, dv))
+    lse = np.zeros((len(rows), H))
+    for r, t in enumerate(rows):
+        o[r], lse[r] = sparse_attention_row(q64[t], kv64, ids[t], scale, dv)
+    return o, lse
