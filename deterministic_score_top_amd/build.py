@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libdsa_indexer.so")
-SOURCES = ["dsa_indexer.hip", "score_kernel.hip", "select_kernel.hip", "backward_kernel.hip"]
+SOURCES = ["dsa_indexer.hip", "score_kernel.hip", "select_kernel.hip", "backward_kernel.hip",
+           "attention_kernel.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

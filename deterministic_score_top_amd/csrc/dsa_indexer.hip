@@ -40,6 +40,7 @@ const DeviceInfo* device_info() {
     int bpc = 0;
     if (dsa::score_occupancy(&bpc, dsa::score_smem_limit()) != hipSuccess || bpc < 1) return;
     if (dsa::bwd_prepare() != hipSuccess) return;
+    if (dsa::attn_prepare(dsa::kMaxTopk) != hipSuccess) return;
     info.score_blocks_per_cu = bpc;
     info.ok = true;
     g_info[dev] = info;
@@ -399,6 +400,35 @@ int dsa_indexer_backward(const dsa_indexer_shape* shape, const void* q, const vo
   return dsa_indexer_backward_ex(shape, q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets,
                                  grad_scores, ld_grad, dq, dk, dw, workspace, workspace_bytes,
                                  stream, nullptr);
+}
+
+int dsa_indexer_sparse_attention(int32_t total_q, int32_t total_kv, int32_t topk, const void* q,
+                                 const void* kv, const int32_t* ids, float scale, float* out,
+                                 float* lse, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  if (total_q < 0 || total_kv < 0 || topk < 1 || topk > dsa::kMaxTopk) return DSA_ERR_SHAPE;
+  if ((int64_t)total_kv * dsa::kAttnDqk * 2 > INT32_MAX) return DSA_ERR_SHAPE;
+  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return DSA_ERR_SHAPE;
+  if (!workspace || (total_q > 0 && (!q || !ids || !out || !lse)) || (total_kv > 0 && !kv)) return DSA_ERR_NULL;
+  if (!aligned16(workspace) || (q && !aligned16(q)) || (kv && !aligned16(kv)) || (out && !aligned16(out)) ||
+      (lse && !aligned16(lse)) || (ids && !aligned4(ids)))
+    return DSA_ERR_ALIGN;
+  if (workspace_bytes < (size_t)dsa::kCtrlBytes) return DSA_ERR_WORKSPACE;
+  if (!device_info()) return DSA_ERR_DEVICE;
+  if (total_q == 0) return DSA_OK;
+  dsa::AttnParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.kv = static_cast<const uint16_t*>(kv);
+  p.ids = ids;
+  p.out = out;
+  p.lse = lse;
+  p.ctrl = static_cast<uint32_t*>(workspace);
+  p.T = total_q;
+  p.Tkv = total_kv;
+  p.topk = topk;
+  p.scale = scale;
+  if (dsa::launch_attention(p, stream) != hipSuccess) return DSA_ERR_LAUNCH;
+  return DSA_OK;
 }
 
 int dsa_indexer_read_status(const void* workspace, hipStream_t stream, uint32_t* status,

@@ -102,6 +102,28 @@ hipError_t bwd_prepare();
 hipError_t launch_backward(const BwdParams& p, int dq_grid, int dk_grid, int cus, hipStream_t s,
                            hipEvent_t between);
 
+// Sparse attention over the selected ids (the selection's consumer).
+constexpr int kAttnThreads = 512;
+constexpr int kAttnTile = 32;    // ids per LDS tile
+constexpr int kAttnHeads = 128;
+constexpr int kAttnDqk = 576;    // latent row (key) dims
+constexpr int kAttnDv = 512;     // value dims: the leading part of the latent row
+constexpr uint32_t kStatusBadIds = 0x8u;
+
+struct AttnParams {
+  const uint16_t* q;   // bf16 [T, 128, 576]
+  const uint16_t* kv;  // bf16 [Tkv, 576]
+  const int32_t* ids;  // [T, topk], -1 = none
+  float* out;          // fp32 [T, 128, 512]
+  float* lse;          // fp32 [T, 128]
+  uint32_t* ctrl;
+  int32_t T, Tkv, topk;
+  float scale;
+};
+size_t attn_smem_bytes(int topk);
+hipError_t attn_prepare(int max_topk);
+hipError_t launch_attention(const AttnParams& p, hipStream_t s);
+
 // Dynamic LDS bytes of the score kernel for a tile table of `max_tiles` entries.
 size_t score_smem_bytes(int B, int max_tiles);
 size_t score_smem_limit();

@@ -43,7 +43,10 @@ EXPORTED_SYMBOLS = (
     "dsa_indexer_backward_workspace_size",
     "dsa_indexer_backward",
     "dsa_indexer_backward_ex",
+    "dsa_indexer_sparse_attention",
 )
+STATUS_BAD_IDS = 0x8
+ATTN_HEADS, ATTN_QK_DIM, ATTN_V_DIM = 128, 576, 512
 
 
 class Shape(ctypes.Structure):
@@ -109,6 +112,8 @@ def lib():
         L.dsa_indexer_backward.restype = ctypes.c_int
         L.dsa_indexer_backward_ex.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp, vp]
         L.dsa_indexer_backward_ex.restype = ctypes.c_int
+        L.dsa_indexer_sparse_attention.argtypes = [i32, i32, i32, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
+        L.dsa_indexer_sparse_attention.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -325,6 +330,38 @@ def backward(q, k, w, cu_seqlens_q, cu_seqlens_k, grad, q_pos_offsets=None, max_
         rc = lib().dsa_indexer_backward_ex(*args, profiler.handle)
     _check(rc, "dsa_indexer_backward")
     return dq, dk, dw
+
+
+def sparse_attention(q, kv, ids, scale: float, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Attention of each query row over its selected ids: out fp32 [T, 128, 512], lse fp32 [T, 128].
+
+    q bf16 [T, 128, 576]; kv bf16 [Tkv, 576] (value = leading 512 dims); ids int32 [T, topk], -1 = none.
+    """
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    T, Tkv = q.shape[0], kv.shape[0]
+    if ids.dim() != 2 or ids.shape[0] != T:
+        raise ValueError("ids must be [T, topk]")
+    k = ids.shape[1]
+    _require(q, "q", torch.bfloat16, (T, ATTN_HEADS, ATTN_QK_DIM), dev)
+    _require(kv, "kv", torch.bfloat16, (Tkv, ATTN_QK_DIM), dev)
+    _require(ids, "ids", torch.int32, (T, k), dev)
+    if out is None:
+        out = torch.empty((T, ATTN_HEADS, ATTN_V_DIM), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((T, ATTN_HEADS), dtype=torch.float32, device=dev)
+    _require(out, "out", torch.float32, (T, ATTN_HEADS, ATTN_V_DIM), dev)
+    _require(lse, "lse", torch.float32, (T, ATTN_HEADS), dev)
+    if workspace is None:
+        workspace = torch.empty(256, dtype=torch.uint8, device=dev)
+        workspace_init(workspace)
+    rc = lib().dsa_indexer_sparse_attention(int(T), int(Tkv), int(k), _ptr(q), _ptr(kv), _ptr(ids), float(scale),
+                                            _ptr(out), _ptr(lse), _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc, "dsa_indexer_sparse_attention")
+    return out, lse
 
 
 def read_status(workspace: torch.Tensor):

@@ -66,6 +66,8 @@ extern "C" {
 #define DSA_STATUS_BAD_SEGMENTS 0x2u    /* cu_seqlens not 0-based, non-decreasing, ending at T/Tkv */
 #define DSA_STATUS_SEQLEN_BOUND 0x4u    /* a segment has more keys than max_seqlen_k; its
                                            queries see only its first max_seqlen_k keys  */
+#define DSA_STATUS_BAD_IDS 0x8u         /* sparse attention: an id outside [-1, total_kv)
+                                           (skipped like -1)                              */
 
 /* Supported sizes. */
 #define DSA_NUM_HEADS 64
@@ -164,6 +166,34 @@ int dsa_indexer_backward(const dsa_indexer_shape* shape, const void* q, const vo
                          const int32_t* q_pos_offsets, const float* grad_scores, int64_t ld_grad,
                          float* dq, float* dk, float* dw, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
+
+/*
+ * The selection's consumer: sparse attention over each row's selected ids (flashinfer PR #4573
+ * and its DeepSeek-V4 sparse-MLA decode follow-up: the kernel reads the selected key ids,
+ * never dereferences -1, gathers those rows of the shared latent KV table and serves the value
+ * operand from the gathered rows).  For query row t and head h, over the valid ids of row t
+ * (0 <= id < total_kv; -1 and padding are skipped):
+ *     S[h, j]   = scale * q[t, h, :] . kv[id_j, :]
+ *     out[t, h, :] = sum_j softmax_j(S[h, :]) * kv[id_j, 0 .. 511]
+ *     lse[t, h] = log sum_j exp(S[h, j])          (natural log)
+ * A row without a valid id gets out = 0 and lse = -inf.
+ *   q          bf16 [total_q, 128, 576]
+ *   kv         bf16 [total_kv, 576]: latent rows, the value is the leading 512 dims
+ *   ids        int32 [total_q, topk], 1 <= topk <= 2048 (e.g. out_ids of dsa_indexer_topk);
+ *              an id outside [-1, total_kv) is skipped and raises DSA_STATUS_BAD_IDS
+ *   out        fp32 [total_q, 128, 512], lse fp32 [total_q, 128]: fully overwritten
+ *   workspace  the 256-byte control block (dsa_indexer_workspace_init), for the status word
+ * Scores are FP32 products of BF16 operands; the softmax runs in FP32 in the exp2 domain and
+ * the probabilities are rounded to BF16 for the value product (FP32 accumulation).  Every sum
+ * has a fixed order: results are bit-reproducible.  total_kv * 1152 must fit in 31 bits.
+ */
+#define DSA_ATTN_HEADS 128
+#define DSA_ATTN_QK_DIM 576
+#define DSA_ATTN_V_DIM 512
+int dsa_indexer_sparse_attention(int32_t total_q, int32_t total_kv, int32_t topk, const void* q,
+                                 const void* kv, const int32_t* ids, float scale, float* out,
+                                 float* lse, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
 
 /* Text of a DSA_ERR_* code. */
 const char* dsa_indexer_status_string(int code);

@@ -144,3 +144,20 @@ def test_backward_argument_errors():
     assert call(ws_bytes=1000) == -4
     no_k = ix.make_shape(16, 0, 1, 64)
     assert call(dk_=None, shape=no_k) in (0, -6)  # no keys: dk may be NULL
+
+
+def test_sparse_attention_argument_errors():
+    L = ix.lib()
+    V = ctypes.c_void_p
+    q, kv, ids, out, lse, ws = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000
+
+    def call(T=4, Tkv=100, k=16, scale=0.1, q_=q, kv_=kv, ids_=ids, out_=out, lse_=lse, ws_=ws, wsb=256):
+        return L.dsa_indexer_sparse_attention(T, Tkv, k, V(q_), V(kv_), V(ids_), scale, V(out_), V(lse_), V(ws_),
+                                              wsb, None)
+    assert call(k=0) == -3 and call(k=2049) == -3 and call(T=-1) == -3
+    assert call(Tkv=1864136) == -3                 # 1152-byte rows past 31 bits
+    assert call(scale=float("nan")) == -3
+    assert call(ids_=None) == -1 and call(ws_=None) == -1
+    assert call(out_=0x40004) == -2 and call(ids_=0x30002) == -2
+    assert call(wsb=100) == -4
+    assert call(T=0, q_=None, ids_=None, out_=None, lse_=None) in (0, -6)

@@ -1,0 +1,141 @@
+"""GPU parity of the sparse attention over the selected ids (through the C ABI) against the FP64 oracle.
+
+Tolerance, from the arithmetic of the HIP path: the probabilities enter the value product as
+BF16 (8 significant bits, relative error <= 2^-8 per term), so
+    |o_gpu - o| <= 2^-7 * (sum_j p_j |v_jd|) / sum_j p_j  (+ 1e-6 * max|v|)
+covers that rounding, the FP32 scores and the hardware exp2/log2; lse within
+1e-5 * (1 + |lse|) plus the FP32 score error.  The relative RMS error of o must stay below
+2^-8.  Rows with one valid id, and identical keys with a power-of-two count, are exact.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from deterministic_score_top_amd import indexer as ix
+from deterministic_score_top_amd import workloads as W
+from oracle import dsa_oracle as O
+
+pytestmark = pytest.mark.gpu
+DV = 512
+
+
+def _gpu(q, kv, ids, scale, **kw):
+    d = "cuda"
+    o, lse = ix.sparse_attention(q.to(d), kv.to(d), torch.as_tensor(ids, dtype=torch.int32).to(d), scale, **kw)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), lse.cpu().numpy()
+
+
+def _check(q, kv, ids, scale, o, lse):
+    q64, kv64 = q.double().numpy(), kv.double().numpy()
+    ro, rl = O.sparse_attention_rows(q64, kv64, ids, scale, DV)
+    for t in range(len(ids)):
+        valid = ids[t][(ids[t] >= 0) & (ids[t] < kv.shape[0])]
+        if valid.size == 0:
+            assert np.all(o[t] == 0) and np.all(np.isneginf(lse[t])), t
+            continue
+        K = kv64[valid]
+        S = scale * (q64[t] @ K.T)
+        P = np.exp(S - S.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        bound = 2.0 ** -7 * (P @ np.abs(K[:, :DV])) + 1e-6 * np.abs(K[:, :DV]).max()
+        err = np.abs(o[t] - ro[t])
+        assert np.all(err <= bound), (t, float(np.max(err - bound)))
+        serr = abs(scale) * 2.0 ** -16 * (np.abs(q64[t]) @ np.abs(K).T).max()
+        assert np.all(np.abs(lse[t] - rl[t]) <= 1e-5 * (1 + np.abs(rl[t])) + serr), t
+    nr = np.linalg.norm(ro)
+    if nr > 0:
+        assert np.linalg.norm(o - ro) <= 2.0 ** -8 * nr
+
+
+def _ids(T, Tkv, k, seed, minus=0.0):
+    rng = np.random.default_rng(seed)
+    ids = np.stack([np.sort(rng.choice(Tkv, k, replace=False)) for _ in range(T)]).astype(np.int32)
+    if minus:
+        ids[rng.random(ids.shape) < minus] = -1
+    return ids
+
+
+def test_random_rows_with_gaps_and_tail():
+    T, Tkv, k = 21, 3000, 100            # 4 tiles of 32 ids, the last one partial
+    q, kv = W.draw_attention(T, Tkv, seed=1)
+    ids = _ids(T, Tkv, k, 1, minus=0.2)
+    ids[3, :] = -1                      # no valid id
+    ids[4, 1:] = -1                     # one valid id
+    scale = 1.0 / math.sqrt(576)
+    o, lse = _gpu(q, kv, ids, scale)
+    _check(q, kv, ids, scale, o, lse)
+
+
+@pytest.mark.parametrize("k,seed", [(1, 2), (31, 3), (32, 4), (2048, 5)])
+def test_topk_widths(k, seed):
+    T, Tkv = 9, 5000
+    q, kv = W.draw_attention(T, Tkv, seed=seed)
+    ids = _ids(T, Tkv, k, seed)
+    scale = 0.06
+    o, lse = _gpu(q, kv, ids, scale)
+    _check(q, kv, ids, scale, o, lse)
+
+
+def test_single_valid_id_exact():
+    T, Tkv = 6, 400
+    q, kv = W.draw_attention(T, Tkv, seed=6)
+    ids = -np.ones((T, 64), np.int32)
+    for t in range(T):
+        ids[t, (7 * t) % 64] = 13 * t + 5
+    o, _ = _gpu(q, kv, ids, 0.05)
+    kvf = kv.float().numpy()
+    for t in range(T):
+        assert np.array_equal(o[t], np.broadcast_to(kvf[13 * t + 5, :DV], o[t].shape)), t
+
+
+def test_identical_keys_exact_mean():
+    T, Tkv = 4, 300
+    q, kv = W.draw_attention(T, Tkv, seed=7)
+    kv[:] = kv[11]
+    ids = _ids(T, Tkv, 64, 7)                 # 64 equal scores: p = 1 each, o = v exactly
+    o, lse = _gpu(q, kv, ids, 0.05)
+    v = kv[11].float().numpy()[:DV]
+    for t in range(T):
+        assert np.array_equal(o[t], np.broadcast_to(v, o[t].shape)), t
+
+
+def test_ids_from_the_topk_call():
+    # the selection's ids feed the attention: causal rows of 600 keys, top-128 of the indexer
+    wl = W.random_segments([40], [600], [560], topk=128, seed=8)
+    d = "cuda"
+    ids, _ = ix.topk(wl.q.to(d), wl.k.to(d), wl.w.to(d), wl.cu_seqlens_q.to(d), wl.cu_seqlens_k.to(d),
+                     wl.q_pos_offsets.to(d), topk=wl.topk, max_seqlen_k=wl.max_seqlen_k)
+    q, kv = W.draw_attention(wl.T, wl.Tkv, seed=8)
+    o, lse = ix.sparse_attention(q.to(d), kv.to(d), ids, 1.0 / math.sqrt(576))
+    torch.cuda.synchronize()
+    _check(q, kv, ids.cpu().numpy(), 1.0 / math.sqrt(576), o.cpu().numpy(), lse.cpu().numpy())
+
+
+def test_bad_ids_flagged_and_skipped():
+    T, Tkv = 5, 200
+    q, kv = W.draw_attention(T, Tkv, seed=9)
+    ids = _ids(T, Tkv, 40, 9)
+    bad = ids.copy()
+    bad[1, 3] = Tkv + 7
+    bad[2, 0] = -5
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    ix.workspace_init(ws)
+    o, lse = _gpu(q, kv, bad, 0.05, workspace=ws)
+    status, _, _ = ix.read_status(ws)
+    assert status & ix.STATUS_BAD_IDS
+    ref = bad.copy()
+    ref[(ref < 0) | (ref >= Tkv)] = -1
+    _check(q, kv, ref, 0.05, o, lse)
+
+
+def test_bitwise_reproducible():
+    T, Tkv = 11, 2000
+    q, kv = W.draw_attention(T, Tkv, seed=10)
+    ids = _ids(T, Tkv, 300, 10, minus=0.1)
+    a = _gpu(q, kv, ids, 0.04)
+    b = _gpu(q, kv, ids, 0.04)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
