@@ -15,6 +15,7 @@ import csv
 import glob
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -255,6 +256,93 @@ def bench_backward(args):
     print(json.dumps(line), flush=True)
 
 
+ATTN_FLOP_PER_ID = 2 * 128 * 576 + 2 * 128 * 512   # scores and value product of one (query, valid id)
+
+
+def bench_attention(args):
+    """One step = one dsa_indexer_sparse_attention call over the workload's rows, with the ids the
+    indexer selects for that workload (its top-k call runs once, outside the timed region)."""
+    import numpy as np
+    import torch
+    from deterministic_score_top_amd import indexer as ix
+    from deterministic_score_top_amd import workloads as W
+
+    wl = W.make(args.config)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"bench: attention {args.config} T={wl.T} Tkv={wl.Tkv} topk={wl.topk}", file=sys.stderr, flush=True)
+    offs = None if wl.q_pos_offsets is None else wl.q_pos_offsets.to(dev)
+    ids, _ = ix.topk(wl.q.to(dev), wl.k.to(dev), wl.w.to(dev), wl.cu_seqlens_q.to(dev), wl.cu_seqlens_k.to(dev),
+                     offs, topk=wl.topk, max_seqlen_k=wl.max_seqlen_k)
+    q_h, kv_h = W.draw_attention(wl.T, wl.Tkv, seed=2)
+    q, kv = q_h.to(dev), kv_h.to(dev)
+    scale = 1.0 / math.sqrt(576)
+    ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    ix.workspace_init(ws)
+    out = torch.empty((wl.T, 128, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((wl.T, 128), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        ix.sparse_attention(q, kv, ids, scale, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        ix.sparse_attention(q, kv, ids, scale, out=out, lse=lse, workspace=ws)
+        b.record(stream)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    kern = sorted(a.elapsed_time(b) for a, b in ev)
+    k_ms = sum(kern) / len(kern)
+    ids_h = ids.cpu().numpy()
+    valid = int((ids_h >= 0).sum())
+    ms = el * 1000.0 / args.steps
+    eff = ATTN_FLOP_PER_ID * valid / (k_ms * 1e-3) / 1e12
+    print(f"bench: attention {ms:.4f} ms/call, kernel {k_ms:.4f} ms", file=sys.stderr, flush=True)
+    line = {
+        "metric": "sparse attention over the selected ids: queries/s + effective TFLOP/s (frac of BF16 MFMA peak)",
+        "value": wl.T / (ms * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.config, "T": wl.T, "Tkv": wl.Tkv, "topk": wl.topk, "heads": 128,
+                   "qk_dim": 576, "v_dim": 512, "valid_ids": valid,
+                   "ids": "the indexer's top-k of the same workload"},
+        "kernel_ms": k_ms,
+        "roofline": {"bound": "mfma", "kernel": "attention_kernel", "achieved": eff, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": eff / PEAK_BF16_TFLOPS, "flop_per_valid_id": ATTN_FLOP_PER_ID,
+                     "gather_bytes_per_valid_id": 2 * 1152, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import dsa_oracle as O
+        q64, kv64 = q_h.double().numpy(), kv_h.double().numpy()
+        o_h, l_h = out.cpu().numpy(), lse.cpu().numpy()
+        order = np.random.default_rng(0).permutation(wl.T).tolist()
+        done, ok = 0, True
+        t0 = time.perf_counter()
+        for t in order:
+            ro, rl = O.sparse_attention_row(q64[t], kv64, ids_h[t], scale, 512)
+            if np.linalg.norm(o_h[t] - ro) > 2.0 ** -7 * max(np.linalg.norm(ro), 1e-30):
+                ok = False
+            done += 1
+            if time.perf_counter() - t0 > args.cpu_budget:
+                break
+        el = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": done / el, "unit": "queries/s", "cores": os.cpu_count(), "kind": "oracle",
+                                "sample": f"{done} of {wl.T} query rows in a seeded random order, one oracle "
+                                          f"sparse_attention_row call per row, {el:.1f} s, FP64 NumPy"}
+        line["parity_sample_ok"] = ok
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,6 +362,8 @@ def main():
                     help="only run a plain copy of known size (counter calibration)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward of the scores (dq, dk, dw) instead of the top-k call")
+    ap.add_argument("--attention", action="store_true",
+                    help="time the sparse attention over the selected ids instead of the top-k call")
     ap.add_argument("--ingest-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write the score-kernel traffic record from rocprofv3 --pmc output directories")
     args = ap.parse_args()
@@ -290,6 +380,9 @@ def main():
 
     if args.backward:
         bench_backward(args)
+        return
+    if args.attention:
+        bench_attention(args)
         return
 
     import torch

@@ -49,6 +49,7 @@ constexpr int kWaitLgkm = 0xC07F;  // s_waitcnt lgkmcnt(0) (LDS), other counters
 constexpr int kDropOffset = 0x7FFFFFF0;  // past any table the host accepts (total_kv * 1152 < 2^31)
 constexpr int kQkSteps = kAttnDqk / 4 / 16;              // 9 K steps per dim quarter
 constexpr int kBlockHeads = 64;                          // heads per block (two blocks per row)
+constexpr int kXcds = 8;                                 // accelerator dies of the MI355X
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -56,7 +57,9 @@ static_assert(kAttnThreads == 512 && kAttnTile == 32 && kAttnHeads == 128, "layo
 static_assert(kRowChunks % 8 == 0, "swizzle works inside 8-chunk groups");
 
 // LDS layout: stages | ids (padded to whole tiles) | score partials | per-head factors
-constexpr int kPartBytes = kWaves * 16 * 64 * 4;   // 32 KiB
+constexpr int kPartStride = 20;                      // floats per lane: 16 partials + 4 pad
+constexpr int kPartWave = 64 * kPartStride;          // floats per wave
+constexpr int kPartBytes = kWaves * kPartWave * 4;   // 40 KiB
 constexpr int kFacBytes = kWaves * 32 * 4;         // 1 KiB
 
 __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
@@ -102,8 +105,25 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hg = wv >> 2, dq = wv & 3;
   const int n = lane & 31, hf = lane >> 5;
-  const int64_t t = blockIdx.x >> 1;
-  const int h0 = (blockIdx.x & 1) * kBlockHeads + 32 * hg;   // first head of this wave's group
+  // Block -> (row, head half), XCD-aware: blocks are dealt to the 8 XCDs round robin, so block
+  // b runs on XCD b % 8.  Both head halves of a row, and the rows t, t + 8, t + 16, ... (whose
+  // selections overlap), go to the same XCD and share its L2.
+  int64_t t;
+  int half;
+  {
+    const int64_t b = blockIdx.x, grid = gridDim.x;   // grid = 2 * T
+    const int64_t x = b % kXcds, slot = b / kXcds;
+    const int64_t per = grid / kXcds;                  // full rounds of kXcds blocks
+    if (slot < (per & ~(int64_t)1)) {
+      half = (int)(slot & 1);
+      t = (slot >> 1) * kXcds + x;
+    } else {                                           // the tail: plain order
+      const int64_t r = b - (per & ~(int64_t)1) * kXcds;
+      t = ((per & ~(int64_t)1) >> 1) * kXcds + (r >> 1);
+      half = (int)(r & 1);
+    }
+  }
+  const int h0 = half * kBlockHeads + 32 * hg;   // first head of this wave's group
   const int ntile = (p.topk + kAttnTile - 1) / kAttnTile;
   int* const ids = reinterpret_cast<int*>(smem + kStages * kStageBytes);
   float* const part = reinterpret_cast<float*>(smem + kStages * kStageBytes + ntile * kAttnTile * 4);
@@ -193,14 +213,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
 #pragma unroll
     for (int st = 0; st < kQkSteps; ++st)
       sp = mfma(*reinterpret_cast<const bf16x8*>(kb + kro[st & 3] + (st >> 2) * 128), qf[st], sp);
-    float* const mine = part + wv * (16 * 64);
+    // lane l's 16 partials at floats l*20 .. l*20+15 of the wave's region: 16-byte accesses,
+    // 16 consecutive lanes on 16 different 4-bank groups
+    f32x4* const mine = reinterpret_cast<f32x4*>(part + wv * kPartWave + lane * kPartStride);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mine[i * 64 + lane] = sp[i];
+    for (int g4 = 0; g4 < 4; ++g4) mine[g4] = f32x4{sp[4 * g4], sp[4 * g4 + 1], sp[4 * g4 + 2], sp[4 * g4 + 3]};
     // LDS writes done, then meet (a fenced __syncthreads would also wait for the next tile's
     // loads, which must stay in flight)
     __builtin_amdgcn_s_waitcnt(kWaitLgkm);
     asm volatile("s_barrier" ::: "memory");
-    const float* const p0 = part + (4 * hg) * (16 * 64);   // the group's four quarters
+    // the group's four quarters, this lane's 16 partials of each
+    const f32x4* const q0 = reinterpret_cast<const f32x4*>(part + (4 * hg) * kPartWave + lane * kPartStride);
+    constexpr int kQ = kPartWave / 4;   // f32x4 stride between the quarters
     // validity of this lane's 16 keys
     const i32x4* const idv = reinterpret_cast<const i32x4*>(ids + kt * kAttnTile);
     // scores in the exp2 domain, -inf for invalid keys (in place of the partial)
@@ -208,13 +232,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const i32x4 iv = idv[2 * g4 + hf];   // keys 8*g4 + 4*hf .. +3
+      // same fixed tree in all four waves of the group
+      const f32x4 sc = (q0[g4] + q0[kQ + g4]) + (q0[2 * kQ + g4] + q0[3 * kQ + g4]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int i = 4 * g4 + c;
-        // same fixed tree in all four waves of the group
-        const float sc = (p0[i * 64 + lane] + p0[1024 + i * 64 + lane]) +
-                         (p0[2048 + i * 64 + lane] + p0[3072 + i * 64 + lane]);
-        sp[i] = iv[c] >= 0 ? sc * c2 : -__builtin_inff();
+        sp[i] = iv[c] >= 0 ? sc[c] * c2 : -__builtin_inff();
         tmax = fmaxf(tmax, sp[i]);
       }
     }
