@@ -8,21 +8,27 @@
 //     lse[t, h]  = log sum_j exp(S[h, j])
 // 128 heads, 576-dim latent rows (the first 512 are the value), any number of ids per row.
 //
-// Two 512-thread blocks per query row, 64 heads each (so a gathered KV tile serves 64 heads;
-// all 128 in one block would need more than the 256 VGPRs of two waves per SIMD).  Wave w
-// takes heads 32*(w/4) .. +31 of its block and dim quarter w%4: the score product over dims
-// 144*(w%4) .. +143 and the output dims 128*(w%4) .. +127.
+// Two 256-thread blocks per query row, one for each half of the value dims; one wave per SIMD,
+// so each wave may hold 512 registers.  Wave w owns heads 32*w .. +31: its Q block (32 heads x
+// 576 dims, 144 VGPRs) for the whole row and its O block (32 heads x 256 value dims, 128
+// accumulator registers).  Each block computes the full scores of all 128 heads (the score
+// product is done twice per row: holding all 512 value dims as well would need 400 registers
+// of operands and accumulators, more than the compiler can place without spilling), so no
+// partial sums cross waves and the block's waves meet only to rotate the tile stages.
 //   * Tiles of 32 ids: their 576-dim rows land in LDS by buffer loads that write LDS directly
 //     (one 16-byte chunk per lane; an id outside [0, Tkv) becomes an out-of-range offset that
-//     reads zeros), the next tile in flight while the current one is multiplied.
-//   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 (K rows from LDS, Q in VGPRs for the whole
-//     row), so that each lane holds one head's scores of 16 keys; the four dim quarters of
-//     a head group add their partial sums through LDS in one fixed tree ((0+1)+(2+3)).
-//   * Online softmax in the exp2 domain per lane (head), the running maximum shared by the
-//     two lane halves; P rounded to BF16 is the A operand of O += P . V, whose V operand is
-//     read key-major from the gathered tile by ds_read_b64_tr_b16.  The O rescale is skipped
-//     when no head's maximum moved (a multiplication by 1).
+//     reads zeros), four stages, two tiles in flight while one is multiplied.
+//   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 (K rows from LDS, Q in VGPRs; the 36 K steps in
+//     ascending dim order), so that each lane holds one head's scores of 16 keys.
+//   * Online softmax per lane (head) in the exp2 domain.  The reference maximum of a head only
+//     moves when a tile's maximum exceeds it by more than 8 (probabilities stay <= 2^8), so the
+//     O rescale is rare; the result is the same softmax, a different but fixed rounding.
+//   * P rounded to BF16 is the A operand of O += P . V, whose V operand is read key-major from
+//     the gathered tile by ds_read_b64_tr_b16.  The value product of tile j - 1 is issued after
+//     the score product of tile j, so its MFMAs run while the wave computes tile j's softmax.
 //   * Every sum has a fixed order, so results are bit-reproducible.
+
+#include <type_traits>
 
 #include "dsa_internal.h"
 
@@ -31,36 +37,33 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = kAttnThreads / 64;
+constexpr int kWaves = kAttnThreads / 64;                // 4: one per SIMD
 constexpr int kRowChunks = kAttnDqk * 2 / 16;            // 72 16-byte chunks per latent row
 constexpr int kTileSlots = kAttnTile * kRowChunks;       // 2304 chunks per tile
-constexpr int kLoadRounds = (kTileSlots + kAttnThreads - 1) / kAttnThreads;  // 5 loads per wave
-constexpr int kStageBytes = kLoadRounds * kAttnThreads * 16;  // 40 KiB (tail slots land in padding)
-constexpr int kStages = 2;
+constexpr int kLoadRounds = kTileSlots / kAttnThreads;   // 9 loads per lane per tile
+constexpr int kStageBytes = kTileSlots * 16;             // 36 KiB
+constexpr int kStages = 4;
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kWaitVm = 0x0F70;    // s_waitcnt: vector memory counter only (OR in the count)
 constexpr int kWaitLgkm = 0xC07F;  // s_waitcnt lgkmcnt(0) (LDS), other counters not waited
 constexpr int kDropOffset = 0x7FFFFFF0;  // past any table the host accepts (total_kv * 1152 < 2^31)
-constexpr int kQkSteps = kAttnDqk / 4 / 16;              // 9 K steps per dim quarter
-constexpr int kBlockHeads = 64;                          // heads per block (two blocks per row)
+constexpr int kQkSteps = kAttnDqk / 16;                  // 36 K steps of the score product
+constexpr int kDvBlocks = kAttnDv / 2 / 32;              // 8 value column blocks of 32 dims per block
 constexpr int kXcds = 8;                                 // accelerator dies of the MI355X
+constexpr float kLazy = 8.f;                             // log2 slack of the reference maximum
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-static_assert(kAttnThreads == 512 && kAttnTile == 32 && kAttnHeads == 128, "layout assumes 8 waves");
+static_assert(kAttnThreads == 256 && kAttnTile == 32 && kAttnHeads == 32 * kWaves, "one wave per 32 heads");
+static_assert(kTileSlots % kAttnThreads == 0, "whole load rounds per tile");
 static_assert(kRowChunks % 8 == 0, "swizzle works inside 8-chunk groups");
 
-// LDS layout: stages | ids (padded to whole tiles) | score partials | per-head factors
-constexpr int kPartStride = 20;                      // floats per lane: 16 partials + 4 pad
-constexpr int kPartWave = 64 * kPartStride;          // floats per wave
-constexpr int kPartBytes = kWaves * kPartWave * 4;   // 40 KiB
-constexpr int kFacBytes = kWaves * 32 * 4;         // 1 KiB
+constexpr int kFacFloats = kWaves * 32;                  // per-head factors, 32 per wave
 
 __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -99,35 +102,51 @@ __device__ __forceinline__ int toff(int row, int chunk) {
   return row * (kRowChunks * 16) + (((chunk & ~7) | ((chunk ^ tswz(row)) & 7)) << 4);
 }
 
+// The tile stages are separate LDS arrays used with compile-time indices (the tile loop is
+// unrolled by the stage count): the compiler can then tell that a gather into one stage does
+// not write the stage being read, and waits for the vector-memory counter only where the
+// code says so instead of before every LDS read.
+__shared__ __align__(16) unsigned char g_stage0[kStageBytes];
+__shared__ __align__(16) unsigned char g_stage1[kStageBytes];
+__shared__ __align__(16) unsigned char g_stage2[kStageBytes];
+__shared__ __align__(16) unsigned char g_stage3[kStageBytes];
+__shared__ __align__(16) int g_ids[kMaxTopk];
+__shared__ __align__(16) float g_fac[kFacFloats];
+static_assert(kStages == 4, "four stage arrays");
+
+template <int S>
+__device__ __forceinline__ unsigned char* stage() {
+  return S == 0 ? g_stage0 : S == 1 ? g_stage1 : S == 2 ? g_stage2 : g_stage3;
+}
+template <int V>
+using Int = std::integral_constant<int, V>;
+
 __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p) {
-  extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hg = wv >> 2, dq = wv & 3;
   const int n = lane & 31, hf = lane >> 5;
-  // Block -> (row, head half), XCD-aware: blocks are dealt to the 8 XCDs round robin, so block
-  // b runs on XCD b % 8.  Both head halves of a row, and the rows t, t + 8, t + 16, ... (whose
-  // selections overlap), go to the same XCD and share its L2.
+  // Block -> (row, value half), XCD-aware: blocks are dealt to the 8 XCDs round robin, so
+  // block b runs on XCD b % 8.  Both halves of a row (which gather the same rows) run on one
+  // XCD, and each XCD takes a contiguous range of rows, whose selections overlap, so the rows
+  // running together on one XCD share its L2.
   int64_t t;
-  int half;
+  int vh;
   {
-    const int64_t b = blockIdx.x, grid = gridDim.x;   // grid = 2 * T
-    const int64_t x = b % kXcds, slot = b / kXcds;
-    const int64_t per = grid / kXcds;                  // full rounds of kXcds blocks
-    if (slot < (per & ~(int64_t)1)) {
-      half = (int)(slot & 1);
-      t = (slot >> 1) * kXcds + x;
-    } else {                                           // the tail: plain order
-      const int64_t r = b - (per & ~(int64_t)1) * kXcds;
-      t = ((per & ~(int64_t)1) >> 1) * kXcds + (r >> 1);
-      half = (int)(r & 1);
+    const int64_t b = blockIdx.x, per = (int64_t)p.T / kXcds;
+    if (b < 2 * per * kXcds) {
+      const int64_t slot = b / kXcds;
+      t = (b % kXcds) * per + (slot >> 1);
+      vh = (int)(slot & 1);
+    } else {   // the rows past the last full round of 8: plain order
+      const int64_t r = b - 2 * per * kXcds;
+      t = per * kXcds + (r >> 1);
+      vh = (int)(r & 1);
     }
   }
-  const int h0 = half * kBlockHeads + 32 * hg;   // first head of this wave's group
+  const int h0 = 32 * wv;   // first head of this wave
   const int ntile = (p.topk + kAttnTile - 1) / kAttnTile;
-  int* const ids = reinterpret_cast<int*>(smem + kStages * kStageBytes);
-  float* const part = reinterpret_cast<float*>(smem + kStages * kStageBytes + ntile * kAttnTile * 4);
-  float* const fac = part + kPartBytes / 4;
+  int* const ids = g_ids;
+  float* const fac = g_fac;
 
   // the row's ids into LDS (padding past topk = -1); ids outside [-1, Tkv) are flagged and skipped
   {
@@ -143,10 +162,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
     if (bad) atomicOr(p.ctrl + kCtrlStatus, kStatusBadIds);
   }
 
-  // B operand of S^T = K . Q^T: column = head h0 + n, K elements = dims 144*dq + 16*st + 8*hf ..
+  // B operand of S^T = K . Q^T: column = head h0 + n, K elements = dims 16*st + 8*hf .. +7
   bf16x8 qf[kQkSteps];
   {
-    const uint16_t* qrow = p.q + ((t * kAttnHeads + h0 + n) * kAttnDqk) + 144 * dq + 8 * hf;
+    const uint16_t* qrow = p.q + ((t * kAttnHeads + h0 + n) * kAttnDqk) + 8 * hf;
 #pragma unroll
     for (int st = 0; st < kQkSteps; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 16 * st);
   }
@@ -155,165 +174,281 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
 
   const __amdgpu_buffer_rsrc_t kvrs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.kv), (short)0, p.Tkv * (kAttnDqk * 2), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t nullrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.kv), (short)0, 0, kRsrcWord3);
-  // tile kt into stage s: load r of wave wv fills slots (r*8 + wv)*64 .. +63; slot -> (row, chunk)
-  auto gather = [&](int s, int kt) {
-    unsigned char* const base = smem + s * kStageBytes;
+  // Gather slots: load r of wave wv fills chunk slots (r*4 + wv)*64 .. +63 of a stage; slot ->
+  // (row, position), and the lane fetches the logical chunk the swizzle stores at that position.
+  int gcol[kLoadRounds];   // byte offset of that chunk inside the latent row
+  int grow[kLoadRounds];   // the slot's row of the tile
+#pragma unroll
+  for (int r = 0; r < kLoadRounds; ++r) {
+    const int slot = (r * kWaves + wv) * 64 + lane;
+    const int row = slot / kRowChunks, pos = slot % kRowChunks;
+    grow[r] = row;
+    gcol[r] = ((pos & ~7) | ((pos ^ tswz(row)) & 7)) * 16;
+  }
+  auto gather = [&](unsigned char* base, int kt) __attribute__((always_inline)) {
+    int id[kLoadRounds];
+#pragma unroll
+    for (int r = 0; r < kLoadRounds; ++r) id[r] = ids[kt * kAttnTile + grow[r]];
 #pragma unroll
     for (int r = 0; r < kLoadRounds; ++r) {
-      const int slot = (r * kWaves + wv) * 64 + lane;
-      const int row = slot / kRowChunks, pos = slot % kRowChunks;
-      const int chunk = (pos & ~7) | ((pos ^ tswz(row)) & 7);   // logical chunk stored at pos
-      const bool tail = (r * kWaves + wv) * 64 >= kTileSlots;   // wave-uniform
-      const int id = tail ? -1 : ids[kt * kAttnTile + min(row, kAttnTile - 1)];
-      const int voff = id >= 0 ? id * (kAttnDqk * 2) + chunk * 16 : kDropOffset;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(tail ? nullrs : kvrs,
-                                               (__attribute__((address_space(3))) void*)(base + (r * kWaves + wv) * 1024),
+      const int voff = id[r] >= 0 ? id[r] * (kAttnDqk * 2) + gcol[r] : kDropOffset;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kvrs, (__attribute__((address_space(3))) void*)(base + (r * kWaves + wv) * 1024),
                                                16, voff, 0, 0, 0);
     }
   };
 
   // transposed-read offsets of the V operand: rows (keys) 4*hf + jr (+8), columns (dims)
-  // 128*dq + 32*nb + 16*(G&1) + 4*r .. +3.  The swizzle only touches the low 3 bits of the
+  // 256*vh + 32*nb + 16*(G&1) + 4*r .. +3.  The swizzle only touches the low 3 bits of the
   // chunk index, which repeat every 2 column blocks: blocks nb and nb + 2 are 128 bytes apart.
   int trv1[2], trv2[2];
   {
     const int L4 = lane & 15, jr = L4 >> 2, r = L4 & 3, gs = (lane >> 4) & 1;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const int chunk = 16 * dq + 4 * nb + 2 * gs + (r >> 1);
-      trv1[nb] = toff(4 * hf + jr, chunk) + 8 * (r & 1);
-      trv2[nb] = toff(8 + 4 * hf + jr, chunk) + 8 * (r & 1);
+      const int chunk = 4 * nb + 2 * gs + (r >> 1);
+      trv1[nb] = toff(4 * hf + jr, chunk) + 8 * (r & 1) + vh * 512;
+      trv2[nb] = toff(8 + 4 * hf + jr, chunk) + 8 * (r & 1) + vh * 512;
     }
   }
-  // row-major K reads: row n, chunk 18*dq + 2*st + hf; K steps st and st + 4 are 128 bytes apart
+  // row-major K reads: row n, chunk 2*st + hf; K steps st and st + 4 are 128 bytes apart
   int kro[4];
 #pragma unroll
-  for (int st = 0; st < 4; ++st) kro[st] = toff(n, 18 * dq + 2 * st + hf);
+  for (int st = 0; st < 4; ++st) kro[st] = toff(n, 2 * st + hf);
 
-  f32x16 oa[4];
+  // The per-tile work is scheduled by hand: sched_barrier fences keep the compiler from
+  // hoisting every operand read of a tile (which would need 144 more VGPRs than the wave has),
+  // while the reads of the next chunk still run one chunk ahead of the MFMAs that use them.
+  //
+  // S^T of the tile in stage `kb`; register i: key 8*(i/4) + 4*hf + i%4, head h0 + n.  Nine
+  // chunks of four K steps (ascending dims) on one accumulator.
+  auto scores = [&](const unsigned char* kb) __attribute__((always_inline)) {
+    auto rd = [&](int st) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8*>(kb + kro[st & 3] + (st >> 2) * 128);
+    };
+    f32x16 sp = f32x16{};
+    bf16x8 ka[4], kn[4];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) oa[nb] = f32x16{};
-  float m = -__builtin_inff(), l = 0.f;   // running max (exp2 domain) and sum of this lane's head
+    for (int j = 0; j < 4; ++j) ka[j] = rd(j);
+#pragma unroll
+    for (int c = 0; c < kQkSteps / 4; ++c) {
+      if (c + 1 < kQkSteps / 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kn[j] = rd(4 * (c + 1) + j);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sp = mfma(ka[j], qf[4 * c + j], sp);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ka[j] = kn[j];
+    }
+    return sp;
+  };
+  f32x16 oa[kDvBlocks];
+#pragma unroll
+  for (int nb = 0; nb < kDvBlocks; ++nb) oa[nb] = f32x16{};
 
-  if (ntile > 0) gather(0, 0);
-  for (int kt = 0; kt < ntile; ++kt) {
-    const int cur = kt & 1;
+  float m = -__builtin_inff(), l = 0.f;   // reference max (exp2 domain) and this lane's partial sum
+  // The softmax of a tile from its scores, in eight phases that can be spread between the
+  // MFMAs of the previous tile's value product: phases 0-3 mask and scale keys 4*ph .. +3 and
+  // take their maximum (phase 3 also moves the reference and sets the O factor), phases 4-7
+  // exponentiate them and add them up (phase 7 also updates l and packs P into the BF16 A
+  // operands of the value product).
+  struct Soft {
+    float tmax, psum, alpha, mref;
+    i32x4 iv[4];
+  };
+  auto soft_begin = [&](int kt) __attribute__((always_inline)) {
+    Soft st;
+    st.tmax = -__builtin_inff();
+    st.psum = 0.f;
+    st.alpha = 1.f;
+    st.mref = 0.f;
+    const i32x4* const idv = reinterpret_cast<const i32x4*>(ids + kt * kAttnTile);
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) st.iv[g4] = idv[2 * g4 + hf];   // keys 8*g4 + 4*hf .. +3
+    return st;
+  };
+  auto soft_phase = [&](int ph, f32x16& sp, Soft& st, bf16x8& na0, bf16x8& na1) __attribute__((always_inline)) {
+    if (ph < 4) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int i = 4 * ph + c;
+        sp[i] = st.iv[ph][c] >= 0 ? sp[i] * c2 : -__builtin_inff();
+        st.tmax = fmaxf(st.tmax, sp[i]);
+      }
+      if (ph == 3) {
+        const float tm = half_max(st.tmax);
+        // the reference moves only past the slack (and from -inf to the first valid maximum)
+        const float mnew = tm > m + kLazy ? tm : m;
+        // before the first valid key O and l are 0: nothing to rescale
+        st.alpha = (mnew == m || m == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
+        m = mnew;
+        st.mref = m == -__builtin_inff() ? 0.f : m;   // no valid key yet: every P is 0
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int i = 4 * (ph - 4) + c;
+        sp[i] = __builtin_amdgcn_exp2f(sp[i] - st.mref);   // exp2(-inf) = 0 for invalid keys
+        st.psum += sp[i];
+      }
+      if (ph == 7) {
+        l = l * st.alpha + st.psum;
+        na0 = pack8(sp, 0);
+        na1 = pack8(sp, 1);
+      }
+    }
+  };
+  auto softmax = [&](f32x16 sp, int kt, bf16x8& na0, bf16x8& na1) __attribute__((always_inline)) {
+    Soft st = soft_begin(kt);
+#pragma unroll
+    for (int ph = 0; ph < 8; ++ph) soft_phase(ph, sp, st, na0, na1);
+    return st.alpha;
+  };
+  // O[h, dv] += P[h, key] . V[key, dv] over the tile in stage `kb`, one value column block at a
+  // time with the next block's transposed reads in flight, and the softmax phases of the next
+  // tile between the MFMAs (VALU work that does not depend on them)
+  struct VOp {
+    bf16x8 lo, hi;
+  };
+  auto vread = [&](const unsigned char* kb, int nb) __attribute__((always_inline)) {
+    const int o1 = trv1[nb & 1] + (nb >> 1) * 128, o2 = trv2[nb & 1] + (nb >> 1) * 128;
+    VOp v;
+    v.lo = lds_tr_pair(kb + o1, kb + o2);
+    v.hi = lds_tr_pair(kb + 16 * (kRowChunks * 16) + o1, kb + 16 * (kRowChunks * 16) + o2);
+    return v;
+  };
+  auto value_softmax = [&](const unsigned char* kb, const bf16x8& pa0, const bf16x8& pa1, f32x16 sp, int kt,
+                           bf16x8& na0, bf16x8& na1) __attribute__((always_inline)) {
+    Soft st = soft_begin(kt);
+    VOp cur = vread(kb, 0), nxt;
+    constexpr int kPer = kDvBlocks / 8;   // value column blocks per softmax phase
+#pragma unroll
+    for (int nb = 0; nb < kDvBlocks; ++nb) {
+      if (nb + 1 < kDvBlocks) nxt = vread(kb, nb + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      oa[nb] = mfma(pa0, cur.lo, oa[nb]);
+      oa[nb] = mfma(pa1, cur.hi, oa[nb]);
+      if (nb % kPer == 0) soft_phase(nb / kPer, sp, st, na0, na1);
+      __builtin_amdgcn_sched_barrier(0);
+      cur = nxt;
+    }
+    return st.alpha;
+  };
+  // O *= alpha per head row (rows of lane l: heads 8*(i/4) + 4*hf + i%4, whose factors sit in
+  // lanes of the other layout), skipped when no head of the wave moved its reference
+  auto rescale = [&](float alpha) __attribute__((always_inline)) {
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) == 0) return;
+    if (hf == 0) fac[wv * 32 + n] = alpha;
+    // the factors are read back by the same wave only (no block barrier needed)
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+    const f32x4* fv = reinterpret_cast<const f32x4*>(fac + wv * 32 + 4 * hf);
+    f32x4 a4[4];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) a4[g4] = fv[2 * g4];
+    // O stays in the accumulator registers: each element is read, scaled and written back in
+    // place.  The compiler does not see into the asm, so the MFMA result hazards are covered by
+    // hand: 24 wait states after the last value-product MFMA, 8 before the next MFMA.
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int nb = 0; nb < kDvBlocks; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = oa[nb][i], tmp;
+        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                     : "+a"(x), "=&v"(tmp)
+                     : "v"(a4[i >> 2][i & 3]));
+        oa[nb][i] = x;
+      }
+    asm volatile("s_nop 7" ::: "memory");
+  };
+
+  // Tile kt lives in stage kt % 4.  Step kt: wait for tile kt, barrier (every wave is past step
+  // kt - 1, so tile kt - 2's stage is free), start gathering tile kt + 2 into it, the score
+  // product of tile kt, then the value product of tile kt - 1 interleaved with tile kt's
+  // softmax.  Tiles kt + 1 and kt + 2 stay in flight.
+  bf16x8 pa0, pa1;
+  auto step = [&](auto S_, auto first_, int kt) __attribute__((always_inline)) {
+    constexpr int S = decltype(S_)::value;
+    constexpr bool first = decltype(first_)::value != 0;
     if (kt + 1 < ntile) {
-      gather(cur ^ 1, kt + 1);
       __builtin_amdgcn_s_waitcnt(kWaitVm | kLoadRounds);
     } else {
       __builtin_amdgcn_s_waitcnt(kWaitVm);
     }
     asm volatile("s_barrier" ::: "memory");
-    const unsigned char* const kb = smem + cur * kStageBytes;
-
-    // partial S^T over this wave's dim quarter; register i: key 8*(i/4) + 4*hf + i%4, head n
-    f32x16 sp = f32x16{};
+    if (kt + 2 < ntile) gather(stage<(S + 2) % kStages>(), kt + 2);
+    const f32x16 sp = scores(stage<S>());
+    float alpha;
+    if constexpr (first) {
+      alpha = softmax(sp, kt, pa0, pa1);
+    } else {
+      bf16x8 na0, na1;
+      alpha = value_softmax(stage<(S + kStages - 1) % kStages>(), pa0, pa1, sp, kt, na0, na1);
+      pa0 = na0;
+      pa1 = na1;
+    }
+    rescale(alpha);
+  };
+  if (ntile > 0) gather(stage<0>(), 0);
+  if (ntile > 1) gather(stage<1>(), 1);
+  if (ntile > 0) step(Int<0>{}, Int<1>{}, 0);
+  for (int kt = 1; kt < ntile; kt += kStages) {
+    step(Int<1>{}, Int<0>{}, kt);
+    if (kt + 1 >= ntile) break;
+    step(Int<2>{}, Int<0>{}, kt + 1);
+    if (kt + 2 >= ntile) break;
+    step(Int<3>{}, Int<0>{}, kt + 2);
+    if (kt + 3 >= ntile) break;
+    step(Int<0>{}, Int<0>{}, kt + 3);
+  }
+  // the value product of the last tile
+  if (ntile > 0) {
+    auto last = [&](const unsigned char* kb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int st = 0; st < kQkSteps; ++st)
-      sp = mfma(*reinterpret_cast<const bf16x8*>(kb + kro[st & 3] + (st >> 2) * 128), qf[st], sp);
-    // lane l's 16 partials at floats l*20 .. l*20+15 of the wave's region: 16-byte accesses,
-    // 16 consecutive lanes on 16 different 4-bank groups
-    f32x4* const mine = reinterpret_cast<f32x4*>(part + wv * kPartWave + lane * kPartStride);
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) mine[g4] = f32x4{sp[4 * g4], sp[4 * g4 + 1], sp[4 * g4 + 2], sp[4 * g4 + 3]};
-    // LDS writes done, then meet (a fenced __syncthreads would also wait for the next tile's
-    // loads, which must stay in flight)
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm);
-    asm volatile("s_barrier" ::: "memory");
-    // the group's four quarters, this lane's 16 partials of each
-    const f32x4* const q0 = reinterpret_cast<const f32x4*>(part + (4 * hg) * kPartWave + lane * kPartStride);
-    constexpr int kQ = kPartWave / 4;   // f32x4 stride between the quarters
-    // validity of this lane's 16 keys
-    const i32x4* const idv = reinterpret_cast<const i32x4*>(ids + kt * kAttnTile);
-    // scores in the exp2 domain, -inf for invalid keys (in place of the partial)
-    float tmax = -__builtin_inff();
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const i32x4 iv = idv[2 * g4 + hf];   // keys 8*g4 + 4*hf .. +3
-      // same fixed tree in all four waves of the group
-      const f32x4 sc = (q0[g4] + q0[kQ + g4]) + (q0[2 * kQ + g4] + q0[3 * kQ + g4]);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int i = 4 * g4 + c;
-        sp[i] = iv[c] >= 0 ? sc[c] * c2 : -__builtin_inff();
-        tmax = fmaxf(tmax, sp[i]);
+      for (int nb = 0; nb < kDvBlocks; ++nb) {
+        const VOp v = vread(kb, nb);
+        oa[nb] = mfma(pa0, v.lo, oa[nb]);
+        oa[nb] = mfma(pa1, v.hi, oa[nb]);
       }
+    };
+    switch ((ntile - 1) % kStages) {
+      case 0: last(stage<0>()); break;
+      case 1: last(stage<1>()); break;
+      case 2: last(stage<2>()); break;
+      default: last(stage<3>()); break;
     }
-    tmax = half_max(tmax);
-    const float mnew = fmaxf(m, tmax);
-    const bool moved = mnew != m;
-    float psum = 0.f;
-    // nothing valid yet: every P is 0 (and m, l stay at -inf, 0)
-    const float mref = mnew == -__builtin_inff() ? 0.f : mnew;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sp[i] = __builtin_amdgcn_exp2f(sp[i] - mref);   // exp2(-inf) = 0 for invalid keys
-      psum += sp[i];
-    }
-    // O and l scale by 2^(m - mnew): exactly 1 when the maximum did not move, 0 before the
-    // first valid key
-    const float alpha = !moved ? 1.f : (m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - mnew));
-    l = l * alpha + half_sum(psum);
-    m = mnew;
-    // O *= alpha per head row, skipped when no head of the wave moved its maximum
-    if (__builtin_amdgcn_ballot_w64(moved) != 0) {
-      if (hf == 0) fac[wv * 32 + n] = alpha;
-      // the factors are read back by the same wave only (no block barrier needed)
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm);
-      const f32x4* fv = reinterpret_cast<const f32x4*>(fac + wv * 32 + 4 * hf);
-      f32x4 a4[4];
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) a4[g4] = fv[2 * g4];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oa[nb][i] *= a4[i >> 2][i & 3];
-    }
-    // O[h, dv] += P[h, key] . V[key, dv]
-    const bf16x8 pa0 = pack8(sp, 0), pa1 = pack8(sp, 1);
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int o1 = trv1[nb & 1] + (nb >> 1) * 128, o2 = trv2[nb & 1] + (nb >> 1) * 128;
-      oa[nb] = mfma(pa0, lds_tr_pair(kb + o1, kb + o2), oa[nb]);
-      oa[nb] = mfma(pa1, lds_tr_pair(kb + 16 * (kRowChunks * 16) + o1, kb + 16 * (kRowChunks * 16) + o2), oa[nb]);
-    }
-    asm volatile("s_barrier" ::: "memory");
   }
 
   // o = O / l (0 for a row with no valid id), lse = (m + log2 l) * ln 2
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float lt = half_sum(l);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm);
   if (hf == 0) fac[wv * 32 + n] = inv;
   __builtin_amdgcn_s_waitcnt(kWaitLgkm);
   const f32x4* fv = reinterpret_cast<const f32x4*>(fac + wv * 32 + 4 * hf);
   f32x4 a4[4];
 #pragma unroll
   for (int g4 = 0; g4 < 4; ++g4) a4[g4] = fv[2 * g4];
-  float* const orow = p.out + ((t * kAttnHeads + h0 + 4 * hf) * kAttnDv) + 128 * dq + n;
+  float* const orow = p.out + ((t * kAttnHeads + h0 + 4 * hf) * kAttnDv) + 256 * vh + n;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
+  for (int nb = 0; nb < kDvBlocks; ++nb)
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       orow[(8 * (i >> 2) + (i & 3)) * kAttnDv + 32 * nb] = oa[nb][i] * a4[i >> 2][i & 3];
-  if (dq == 0 && hf == 0)
-    p.lse[t * kAttnHeads + h0 + n] = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -__builtin_inff();
+  if (hf == 0 && vh == 0)
+    p.lse[t * kAttnHeads + h0 + n] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -__builtin_inff();
 }
 
 }  // namespace
 
-size_t attn_smem_bytes(int topk) {
-  const int ntile = (topk + kAttnTile - 1) / kAttnTile;
-  return (size_t)kStages * kStageBytes + (size_t)ntile * kAttnTile * 4 + kPartBytes + kFacBytes;
-}
+size_t attn_smem_bytes(int) { return 0; }   // all LDS is static
 
-hipError_t attn_prepare(int max_topk) {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(attention_kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)attn_smem_bytes(max_topk));
-}
+hipError_t attn_prepare(int) { return hipSuccess; }
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(attention_kernel, dim3(2 * p.T), dim3(kAttnThreads), attn_smem_bytes(p.topk), s, p);
+  hipLaunchKernelGGL(attention_kernel, dim3(2 * p.T), dim3(kAttnThreads), 0, s, p);
   return hipGetLastError();
 }
 
