@@ -8,24 +8,27 @@
 //     lse[t, h]  = log sum_j exp(S[h, j])
 // 128 heads, 576-dim latent rows (the first 512 are the value), any number of ids per row.
 //
-// Two 256-thread blocks per query row, one for each half of the value dims; one wave per SIMD,
-// so each wave may hold 512 registers.  Wave w owns heads 32*w .. +31: its Q block (32 heads x
-// 576 dims, 144 VGPRs) for the whole row and its O block (32 heads x 256 value dims, 128
-// accumulator registers).  Each block computes the full scores of all 128 heads (the score
-// product is done twice per row: holding all 512 value dims as well would need 400 registers
-// of operands and accumulators, more than the compiler can place without spilling), so no
-// partial sums cross waves and the block's waves meet only to rotate the tile stages.
-//   * Tiles of 32 ids: their 576-dim rows land in LDS by buffer loads that write LDS directly
-//     (one 16-byte chunk per lane; an id outside [0, Tkv) becomes an out-of-range offset that
-//     reads zeros), four stages, two tiles in flight while one is multiplied.
-//   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 (K rows from LDS, Q in VGPRs; the 36 K steps in
-//     ascending dim order), so that each lane holds one head's scores of 16 keys.
+// Two 256-thread blocks per query row, one per half of the heads; one wave per SIMD, so each
+// wave may hold 512 registers.  Tiles of 64 ids.  Wave w = (head group g = w % 2, key half
+// c = w / 2) owns heads 64*half + 32*g .. +31:
+//   * its Q block (32 heads x 576 dims, 144 registers) for the whole row;
+//   * the scores of the tile's keys 32*c .. +31 (S^T = K . Q^T on v_mfma_f32_32x32x16_bf16, K
+//     rows from LDS, the 36 K steps in ascending dim order): each score is computed once;
+//   * the O block of its heads and value half c (32 heads x 256 dims, 128 accumulator
+//     registers) over all 64 keys of the tile, with P of the other key half taken from the
+//     partner wave (same heads, other key half) through LDS.
+// Per tile the pair agrees on each head's maximum (exchanged through LDS), so both apply the
+// same softmax reference; the O rows and the partial sums l of a head stay consistent.
+//   * Gathered rows land in LDS by buffer loads that write LDS directly (one 16-byte chunk per
+//     lane; an id outside [0, Tkv) becomes an out-of-range offset that reads zeros), two
+//     stages: the next tile is in flight while one is multiplied.
+//   * Once every wave has finished its score product, the last 64 dims of the tile's rows
+//     (needed only for the scores) hold the P exchange.
 //   * Online softmax per lane (head) in the exp2 domain.  The reference maximum of a head only
 //     moves when a tile's maximum exceeds it by more than 8 (probabilities stay <= 2^8), so the
 //     O rescale is rare; the result is the same softmax, a different but fixed rounding.
 //   * P rounded to BF16 is the A operand of O += P . V, whose V operand is read key-major from
-//     the gathered tile by ds_read_b64_tr_b16.  The value product of tile j - 1 is issued after
-//     the score product of tile j, so its MFMAs run while the wave computes tile j's softmax.
+//     the gathered tile by ds_read_b64_tr_b16.
 //   * Every sum has a fixed order, so results are bit-reproducible.
 
 #include <type_traits>
@@ -44,26 +47,24 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = kAttnThreads / 64;                // 4: one per SIMD
 constexpr int kRowChunks = kAttnDqk * 2 / 16;            // 72 16-byte chunks per latent row
-constexpr int kTileSlots = kAttnTile * kRowChunks;       // 2304 chunks per tile
-constexpr int kLoadRounds = kTileSlots / kAttnThreads;   // 9 loads per lane per tile
-constexpr int kStageBytes = kTileSlots * 16;             // 36 KiB
-constexpr int kStages = 4;
+constexpr int kRowBytes = kAttnDqk * 2;                  // 1152
+constexpr int kTileSlots = kAttnTile * kRowChunks;       // 4608 chunks per tile
+constexpr int kLoadRounds = kTileSlots / kAttnThreads;   // 18 loads per lane per tile
+constexpr int kStageBytes = kTileSlots * 16;             // 72 KiB
 constexpr int kRsrcWord3 = 0x00020000;
-constexpr int kWaitVm = 0x0F70;    // s_waitcnt: vector memory counter only (OR in the count)
 constexpr int kWaitLgkm = 0xC07F;  // s_waitcnt lgkmcnt(0) (LDS), other counters not waited
 constexpr int kDropOffset = 0x7FFFFFF0;  // past any table the host accepts (total_kv * 1152 < 2^31)
 constexpr int kQkSteps = kAttnDqk / 16;                  // 36 K steps of the score product
-constexpr int kDvBlocks = kAttnDv / 2 / 32;              // 8 value column blocks of 32 dims per block
+constexpr int kDvBlocks = kAttnDv / 2 / 32;              // 8 value column blocks of 32 dims per wave
 constexpr int kXcds = 8;                                 // accelerator dies of the MI355X
 constexpr float kLazy = 8.f;                             // log2 slack of the reference maximum
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-static_assert(kAttnThreads == 256 && kAttnTile == 32 && kAttnHeads == 32 * kWaves, "one wave per 32 heads");
+static_assert(kAttnThreads == 256 && kAttnTile == 64 && kAttnHeads == 2 * 2 * 32, "4 waves x 32 heads x 2 blocks");
 static_assert(kTileSlots % kAttnThreads == 0, "whole load rounds per tile");
 static_assert(kRowChunks % 8 == 0, "swizzle works inside 8-chunk groups");
-
-constexpr int kFacFloats = kWaves * 32;                  // per-head factors, 32 per wave
+static_assert(kWaves * 64 * 32 <= kAttnTile * (kRowBytes - kAttnDv * 2), "the P exchange fits the rope dims");
 
 __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -102,21 +103,19 @@ __device__ __forceinline__ int toff(int row, int chunk) {
   return row * (kRowChunks * 16) + (((chunk & ~7) | ((chunk ^ tswz(row)) & 7)) << 4);
 }
 
-// The tile stages are separate LDS arrays used with compile-time indices (the tile loop is
-// unrolled by the stage count): the compiler can then tell that a gather into one stage does
-// not write the stage being read, and waits for the vector-memory counter only where the
-// code says so instead of before every LDS read.
+// The two tile stages are separate LDS arrays used with compile-time indices (the tile loop is
+// unrolled by two): the compiler can then tell that a gather into one stage does not write the
+// stage being read, and waits for the vector-memory counter only where the code says so
+// instead of before every LDS read.
 __shared__ __align__(16) unsigned char g_stage0[kStageBytes];
 __shared__ __align__(16) unsigned char g_stage1[kStageBytes];
-__shared__ __align__(16) unsigned char g_stage2[kStageBytes];
-__shared__ __align__(16) unsigned char g_stage3[kStageBytes];
 __shared__ __align__(16) int g_ids[kMaxTopk];
-__shared__ __align__(16) float g_fac[kFacFloats];
-static_assert(kStages == 4, "four stage arrays");
+__shared__ __align__(16) float g_xchg[kWaves * 32];   // per-head maxima, then partial sums
+__shared__ __align__(16) float g_fac[kWaves * 32];    // per-head factors of each wave
 
 template <int S>
 __device__ __forceinline__ unsigned char* stage() {
-  return S == 0 ? g_stage0 : S == 1 ? g_stage1 : S == 2 ? g_stage2 : g_stage3;
+  return S == 0 ? g_stage0 : g_stage1;
 }
 template <int V>
 using Int = std::integral_constant<int, V>;
@@ -124,29 +123,29 @@ using Int = std::integral_constant<int, V>;
 __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hg = wv & 1, kh = wv >> 1, partner = wv ^ 2;
   const int n = lane & 31, hf = lane >> 5;
-  // Block -> (row, value half), XCD-aware: blocks are dealt to the 8 XCDs round robin, so
-  // block b runs on XCD b % 8.  Both halves of a row (which gather the same rows) run on one
-  // XCD, and each XCD takes a contiguous range of rows, whose selections overlap, so the rows
-  // running together on one XCD share its L2.
+  // Block -> (row, head half), XCD-aware: blocks are dealt to the 8 XCDs round robin, so block
+  // b runs on XCD b % 8.  Both halves of a row (which gather the same rows) run on one XCD, and
+  // each XCD takes a contiguous range of rows, whose selections overlap, so the rows running
+  // together on one XCD share its L2.
   int64_t t;
-  int vh;
+  int half;
   {
     const int64_t b = blockIdx.x, per = (int64_t)p.T / kXcds;
     if (b < 2 * per * kXcds) {
       const int64_t slot = b / kXcds;
       t = (b % kXcds) * per + (slot >> 1);
-      vh = (int)(slot & 1);
+      half = (int)(slot & 1);
     } else {   // the rows past the last full round of 8: plain order
       const int64_t r = b - 2 * per * kXcds;
       t = per * kXcds + (r >> 1);
-      vh = (int)(r & 1);
+      half = (int)(r & 1);
     }
   }
-  const int h0 = 32 * wv;   // first head of this wave
+  const int h0 = 64 * half + 32 * hg;   // first head of this wave
   const int ntile = (p.topk + kAttnTile - 1) / kAttnTile;
   int* const ids = g_ids;
-  float* const fac = g_fac;
 
   // the row's ids into LDS (padding past topk = -1); ids outside [-1, Tkv) are flagged and skipped
   {
@@ -173,32 +172,26 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
   __syncthreads();
 
   const __amdgpu_buffer_rsrc_t kvrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.kv), (short)0, p.Tkv * (kAttnDqk * 2), kRsrcWord3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.kv), (short)0, p.Tkv * kRowBytes, kRsrcWord3);
   // Gather slots: load r of wave wv fills chunk slots (r*4 + wv)*64 .. +63 of a stage; slot ->
   // (row, position), and the lane fetches the logical chunk the swizzle stores at that position.
-  int gcol[kLoadRounds];   // byte offset of that chunk inside the latent row
-  int grow[kLoadRounds];   // the slot's row of the tile
-#pragma unroll
-  for (int r = 0; r < kLoadRounds; ++r) {
-    const int slot = (r * kWaves + wv) * 64 + lane;
-    const int row = slot / kRowChunks, pos = slot % kRowChunks;
-    grow[r] = row;
-    gcol[r] = ((pos & ~7) | ((pos ^ tswz(row)) & 7)) * 16;
-  }
   auto gather = [&](unsigned char* base, int kt) __attribute__((always_inline)) {
     int id[kLoadRounds];
 #pragma unroll
-    for (int r = 0; r < kLoadRounds; ++r) id[r] = ids[kt * kAttnTile + grow[r]];
+    for (int r = 0; r < kLoadRounds; ++r) id[r] = ids[kt * kAttnTile + ((r * kWaves + wv) * 64 + lane) / kRowChunks];
 #pragma unroll
     for (int r = 0; r < kLoadRounds; ++r) {
-      const int voff = id[r] >= 0 ? id[r] * (kAttnDqk * 2) + gcol[r] : kDropOffset;
+      const int slot = (r * kWaves + wv) * 64 + lane;
+      const int row = slot / kRowChunks, pos = slot - row * kRowChunks;
+      const int col = ((pos & ~7) | ((pos ^ tswz(row)) & 7)) * 16;
+      const int voff = id[r] >= 0 ? id[r] * kRowBytes + col : kDropOffset;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(kvrs, (__attribute__((address_space(3))) void*)(base + (r * kWaves + wv) * 1024),
                                                16, voff, 0, 0, 0);
     }
   };
 
   // transposed-read offsets of the V operand: rows (keys) 4*hf + jr (+8), columns (dims)
-  // 256*vh + 32*nb + 16*(G&1) + 4*r .. +3.  The swizzle only touches the low 3 bits of the
+  // 256*kh + 32*nb + 16*(G&1) + 4*r .. +3.  The swizzle only touches the low 3 bits of the
   // chunk index, which repeat every 2 column blocks: blocks nb and nb + 2 are 128 bytes apart.
   int trv1[2], trv2[2];
   {
@@ -206,21 +199,25 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int chunk = 4 * nb + 2 * gs + (r >> 1);
-      trv1[nb] = toff(4 * hf + jr, chunk) + 8 * (r & 1) + vh * 512;
-      trv2[nb] = toff(8 + 4 * hf + jr, chunk) + 8 * (r & 1) + vh * 512;
+      trv1[nb] = toff(4 * hf + jr, chunk) + 8 * (r & 1) + kh * 512;
+      trv2[nb] = toff(8 + 4 * hf + jr, chunk) + 8 * (r & 1) + kh * 512;
     }
   }
-  // row-major K reads: row n, chunk 2*st + hf; K steps st and st + 4 are 128 bytes apart
+  // row-major K reads: row 32*kh + n, chunk 2*st + hf; K steps st and st + 4 are 128 bytes apart
+  // (row 32*kh + n has the swizzle of row n)
   int kro[4];
 #pragma unroll
-  for (int st = 0; st < 4; ++st) kro[st] = toff(n, 2 * st + hf);
+  for (int st = 0; st < 4; ++st) kro[st] = toff(n, 2 * st + hf) + 32 * kh * kRowBytes;
+  // P exchange slots in the rope dims: wave w's lane l at row 16*w + l/4, bytes 1024 + 32*(l%4)
+  const int xown = (16 * wv + (lane >> 2)) * kRowBytes + kAttnDv * 2 + 32 * (lane & 3);
+  const int xpar = (16 * partner + (lane >> 2)) * kRowBytes + kAttnDv * 2 + 32 * (lane & 3);
 
   // The per-tile work is scheduled by hand: sched_barrier fences keep the compiler from
-  // hoisting every operand read of a tile (which would need 144 more VGPRs than the wave has),
-  // while the reads of the next chunk still run one chunk ahead of the MFMAs that use them.
+  // hoisting every operand read of a tile into registers, while the reads of the next chunk
+  // still run one chunk ahead of the MFMAs that use them.
   //
-  // S^T of the tile in stage `kb`; register i: key 8*(i/4) + 4*hf + i%4, head h0 + n.  Nine
-  // chunks of four K steps (ascending dims) on one accumulator.
+  // S^T of this wave's 32 keys; register i: key 32*kh + 8*(i/4) + 4*hf + i%4, head h0 + n.
+  // Nine chunks of four K steps (ascending dims) on one accumulator.
   auto scores = [&](const unsigned char* kb) __attribute__((always_inline)) {
     auto rd = [&](int st) __attribute__((always_inline)) {
       return *reinterpret_cast<const bf16x8*>(kb + kro[st & 3] + (st >> 2) * 128);
@@ -247,103 +244,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
   f32x16 oa[kDvBlocks];
 #pragma unroll
   for (int nb = 0; nb < kDvBlocks; ++nb) oa[nb] = f32x16{};
-
   float m = -__builtin_inff(), l = 0.f;   // reference max (exp2 domain) and this lane's partial sum
-  // The softmax of a tile from its scores, in eight phases that can be spread between the
-  // MFMAs of the previous tile's value product: phases 0-3 mask and scale keys 4*ph .. +3 and
-  // take their maximum (phase 3 also moves the reference and sets the O factor), phases 4-7
-  // exponentiate them and add them up (phase 7 also updates l and packs P into the BF16 A
-  // operands of the value product).
-  struct Soft {
-    float tmax, psum, alpha, mref;
-    i32x4 iv[4];
-  };
-  auto soft_begin = [&](int kt) __attribute__((always_inline)) {
-    Soft st;
-    st.tmax = -__builtin_inff();
-    st.psum = 0.f;
-    st.alpha = 1.f;
-    st.mref = 0.f;
-    const i32x4* const idv = reinterpret_cast<const i32x4*>(ids + kt * kAttnTile);
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) st.iv[g4] = idv[2 * g4 + hf];   // keys 8*g4 + 4*hf .. +3
-    return st;
-  };
-  auto soft_phase = [&](int ph, f32x16& sp, Soft& st, bf16x8& na0, bf16x8& na1) __attribute__((always_inline)) {
-    if (ph < 4) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int i = 4 * ph + c;
-        sp[i] = st.iv[ph][c] >= 0 ? sp[i] * c2 : -__builtin_inff();
-        st.tmax = fmaxf(st.tmax, sp[i]);
-      }
-      if (ph == 3) {
-        const float tm = half_max(st.tmax);
-        // the reference moves only past the slack (and from -inf to the first valid maximum)
-        const float mnew = tm > m + kLazy ? tm : m;
-        // before the first valid key O and l are 0: nothing to rescale
-        st.alpha = (mnew == m || m == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
-        m = mnew;
-        st.mref = m == -__builtin_inff() ? 0.f : m;   // no valid key yet: every P is 0
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int i = 4 * (ph - 4) + c;
-        sp[i] = __builtin_amdgcn_exp2f(sp[i] - st.mref);   // exp2(-inf) = 0 for invalid keys
-        st.psum += sp[i];
-      }
-      if (ph == 7) {
-        l = l * st.alpha + st.psum;
-        na0 = pack8(sp, 0);
-        na1 = pack8(sp, 1);
-      }
-    }
-  };
-  auto softmax = [&](f32x16 sp, int kt, bf16x8& na0, bf16x8& na1) __attribute__((always_inline)) {
-    Soft st = soft_begin(kt);
-#pragma unroll
-    for (int ph = 0; ph < 8; ++ph) soft_phase(ph, sp, st, na0, na1);
-    return st.alpha;
-  };
-  // O[h, dv] += P[h, key] . V[key, dv] over the tile in stage `kb`, one value column block at a
-  // time with the next block's transposed reads in flight, and the softmax phases of the next
-  // tile between the MFMAs (VALU work that does not depend on them)
-  struct VOp {
-    bf16x8 lo, hi;
-  };
-  auto vread = [&](const unsigned char* kb, int nb) __attribute__((always_inline)) {
-    const int o1 = trv1[nb & 1] + (nb >> 1) * 128, o2 = trv2[nb & 1] + (nb >> 1) * 128;
-    VOp v;
-    v.lo = lds_tr_pair(kb + o1, kb + o2);
-    v.hi = lds_tr_pair(kb + 16 * (kRowChunks * 16) + o1, kb + 16 * (kRowChunks * 16) + o2);
-    return v;
-  };
-  auto value_softmax = [&](const unsigned char* kb, const bf16x8& pa0, const bf16x8& pa1, f32x16 sp, int kt,
-                           bf16x8& na0, bf16x8& na1) __attribute__((always_inline)) {
-    Soft st = soft_begin(kt);
-    VOp cur = vread(kb, 0), nxt;
-    constexpr int kPer = kDvBlocks / 8;   // value column blocks per softmax phase
-#pragma unroll
-    for (int nb = 0; nb < kDvBlocks; ++nb) {
-      if (nb + 1 < kDvBlocks) nxt = vread(kb, nb + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      oa[nb] = mfma(pa0, cur.lo, oa[nb]);
-      oa[nb] = mfma(pa1, cur.hi, oa[nb]);
-      if (nb % kPer == 0) soft_phase(nb / kPer, sp, st, na0, na1);
-      __builtin_amdgcn_sched_barrier(0);
-      cur = nxt;
-    }
-    return st.alpha;
-  };
+
   // O *= alpha per head row (rows of lane l: heads 8*(i/4) + 4*hf + i%4, whose factors sit in
   // lanes of the other layout), skipped when no head of the wave moved its reference
   auto rescale = [&](float alpha) __attribute__((always_inline)) {
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f) == 0) return;
-    if (hf == 0) fac[wv * 32 + n] = alpha;
+    if (hf == 0) g_fac[wv * 32 + n] = alpha;
     // the factors are read back by the same wave only (no block barrier needed)
     __builtin_amdgcn_s_waitcnt(kWaitLgkm);
-    const f32x4* fv = reinterpret_cast<const f32x4*>(fac + wv * 32 + 4 * hf);
+    const f32x4* fv = reinterpret_cast<const f32x4*>(g_fac + wv * 32 + 4 * hf);
     f32x4 a4[4];
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) a4[g4] = fv[2 * g4];
@@ -364,80 +274,113 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
     asm volatile("s_nop 7" ::: "memory");
   };
 
-  // Tile kt lives in stage kt % 4.  Step kt: wait for tile kt, barrier (every wave is past step
-  // kt - 1, so tile kt - 2's stage is free), start gathering tile kt + 2 into it, the score
-  // product of tile kt, then the value product of tile kt - 1 interleaved with tile kt's
-  // softmax.  Tiles kt + 1 and kt + 2 stay in flight.
-  bf16x8 pa0, pa1;
-  auto step = [&](auto S_, auto first_, int kt) __attribute__((always_inline)) {
+  // Step kt (tile kt in stage kt % 2): wait for tile kt and meet (every wave is past step
+  // kt - 1, so the other stage is free) and start gathering tile kt + 1 into it; scores of this
+  // wave's keys; meet to exchange the per-head maxima; P of this wave's keys into the rope dims;
+  // meet; the value product over all 64 keys with the partner's P.
+  auto step = [&](auto S_, int kt) __attribute__((always_inline)) {
     constexpr int S = decltype(S_)::value;
-    constexpr bool first = decltype(first_)::value != 0;
-    if (kt + 1 < ntile) {
-      __builtin_amdgcn_s_waitcnt(kWaitVm | kLoadRounds);
-    } else {
-      __builtin_amdgcn_s_waitcnt(kWaitVm);
-    }
+    unsigned char* const kb = stage<S>();
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vector memory counter 0: tile kt has landed
     asm volatile("s_barrier" ::: "memory");
-    if (kt + 2 < ntile) gather(stage<(S + 2) % kStages>(), kt + 2);
-    const f32x16 sp = scores(stage<S>());
-    float alpha;
-    if constexpr (first) {
-      alpha = softmax(sp, kt, pa0, pa1);
-    } else {
-      bf16x8 na0, na1;
-      alpha = value_softmax(stage<(S + kStages - 1) % kStages>(), pa0, pa1, sp, kt, na0, na1);
-      pa0 = na0;
-      pa1 = na1;
+    if (kt + 1 < ntile) gather(stage<1 - S>(), kt + 1);
+    f32x16 sp = scores(kb);
+
+    // mask, scale and the maximum of each head over this wave's keys
+    const i32x4* const idv = reinterpret_cast<const i32x4*>(ids + kt * kAttnTile + 32 * kh);
+    float tmax = -__builtin_inff();
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const i32x4 iv = idv[2 * g4 + hf];   // keys 32*kh + 8*g4 + 4*hf .. +3
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int i = 4 * g4 + c;
+        sp[i] = iv[c] >= 0 ? sp[i] * c2 : -__builtin_inff();
+        tmax = fmaxf(tmax, sp[i]);
+      }
     }
+    tmax = half_max(tmax);
+    if (hf == 0) g_xchg[wv * 32 + n] = tmax;
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+    asm volatile("s_barrier" ::: "memory");
+    tmax = fmaxf(tmax, g_xchg[partner * 32 + n]);   // the pair's maximum: equal in both waves
+    // the reference moves only past the slack (and from -inf to the first valid maximum)
+    const float mnew = tmax > m + kLazy ? tmax : m;
+    // before the first valid key O and l are 0: nothing to rescale
+    const float alpha = (mnew == m || m == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
+    m = mnew;
+    const float mref = m == -__builtin_inff() ? 0.f : m;   // no valid key yet: every P is 0
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sp[i] = __builtin_amdgcn_exp2f(sp[i] - mref);   // exp2(-inf) = 0 for invalid keys
+      psum += sp[i];
+    }
+    l = l * alpha + psum;
+    const bf16x8 pa0 = pack8(sp, 0), pa1 = pack8(sp, 1);
+    // every wave's score product is done (the maxima were written after it): the rope dims of
+    // this stage are free for the P exchange
+    *reinterpret_cast<bf16x8*>(kb + xown) = pa0;
+    *reinterpret_cast<bf16x8*>(kb + xown + 16) = pa1;
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+    asm volatile("s_barrier" ::: "memory");
+    const bf16x8 qa0 = *reinterpret_cast<const bf16x8*>(kb + xpar);
+    const bf16x8 qa1 = *reinterpret_cast<const bf16x8*>(kb + xpar + 16);
     rescale(alpha);
+    // P of key half 0 then key half 1 (keys ascending), K steps of 16 keys
+    const bf16x8 pk[4] = {kh == 0 ? pa0 : qa0, kh == 0 ? pa1 : qa1, kh == 0 ? qa0 : pa0, kh == 0 ? qa1 : pa1};
+    auto vread = [&](int nb, int j) __attribute__((always_inline)) {
+      const int o1 = trv1[nb & 1] + (nb >> 1) * 128 + 16 * j * kRowBytes;
+      const int o2 = trv2[nb & 1] + (nb >> 1) * 128 + 16 * j * kRowBytes;
+      return lds_tr_pair(kb + o1, kb + o2);
+    };
+    bf16x8 va[4], vn[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) va[j] = vread(0, j);
+#pragma unroll
+    for (int nb = 0; nb < kDvBlocks; ++nb) {
+      if (nb + 1 < kDvBlocks) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vn[j] = vread(nb + 1, j);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) oa[nb] = mfma(pk[j], va[j], oa[nb]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) va[j] = vn[j];
+    }
   };
   if (ntile > 0) gather(stage<0>(), 0);
-  if (ntile > 1) gather(stage<1>(), 1);
-  if (ntile > 0) step(Int<0>{}, Int<1>{}, 0);
-  for (int kt = 1; kt < ntile; kt += kStages) {
-    step(Int<1>{}, Int<0>{}, kt);
+  for (int kt = 0; kt < ntile; kt += 2) {
+    step(Int<0>{}, kt);
     if (kt + 1 >= ntile) break;
-    step(Int<2>{}, Int<0>{}, kt + 1);
-    if (kt + 2 >= ntile) break;
-    step(Int<3>{}, Int<0>{}, kt + 2);
-    if (kt + 3 >= ntile) break;
-    step(Int<0>{}, Int<0>{}, kt + 3);
-  }
-  // the value product of the last tile
-  if (ntile > 0) {
-    auto last = [&](const unsigned char* kb) __attribute__((always_inline)) {
-#pragma unroll
-      for (int nb = 0; nb < kDvBlocks; ++nb) {
-        const VOp v = vread(kb, nb);
-        oa[nb] = mfma(pa0, v.lo, oa[nb]);
-        oa[nb] = mfma(pa1, v.hi, oa[nb]);
-      }
-    };
-    switch ((ntile - 1) % kStages) {
-      case 0: last(stage<0>()); break;
-      case 1: last(stage<1>()); break;
-      case 2: last(stage<2>()); break;
-      default: last(stage<3>()); break;
-    }
+    step(Int<1>{}, kt + 1);
   }
 
-  // o = O / l (0 for a row with no valid id), lse = (m + log2 l) * ln 2
-  const float lt = half_sum(l);
+  // l of each head = the pair's partial sums, key half 0 first; o = O / l (0 for a row with no
+  // valid id), lse = (m + log2 l) * ln 2.  Every read of the exchanged maxima happened before
+  // the last step's final barrier.
+  const float lw = half_sum(l);
+  if (hf == 0) g_xchg[wv * 32 + n] = lw;
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+  __syncthreads();
+  const float lp = g_xchg[partner * 32 + n];
+  const float lt = kh == 0 ? lw + lp : lp + lw;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (hf == 0) g_fac[wv * 32 + n] = inv;
   __builtin_amdgcn_s_waitcnt(kWaitLgkm);
-  if (hf == 0) fac[wv * 32 + n] = inv;
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm);
-  const f32x4* fv = reinterpret_cast<const f32x4*>(fac + wv * 32 + 4 * hf);
+  const f32x4* fv = reinterpret_cast<const f32x4*>(g_fac + wv * 32 + 4 * hf);
   f32x4 a4[4];
 #pragma unroll
   for (int g4 = 0; g4 < 4; ++g4) a4[g4] = fv[2 * g4];
-  float* const orow = p.out + ((t * kAttnHeads + h0 + 4 * hf) * kAttnDv) + 256 * vh + n;
+  float* const orow = p.out + ((t * kAttnHeads + h0 + 4 * hf) * kAttnDv) + 256 * kh + n;
 #pragma unroll
   for (int nb = 0; nb < kDvBlocks; ++nb)
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       orow[(8 * (i >> 2) + (i & 3)) * kAttnDv + 32 * nb] = oa[nb][i] * a4[i >> 2][i & 3];
-  if (hf == 0 && vh == 0)
+  if (hf == 0 && kh == 0)
     p.lse[t * kAttnHeads + h0 + n] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -__builtin_inff();
 }
 

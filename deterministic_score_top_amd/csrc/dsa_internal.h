@@ -104,7 +104,7 @@ hipError_t launch_backward(const BwdParams& p, int dq_grid, int dk_grid, int cus
 
 // Sparse attention over the selected ids (the selection's consumer).
 constexpr int kAttnThreads = 256;
-constexpr int kAttnTile = 32;    // ids per LDS tile
+constexpr int kAttnTile = 64;    // ids per LDS tile
 constexpr int kAttnHeads = 128;
 constexpr int kAttnDqk = 576;    // latent row (key) dims
 constexpr int kAttnDv = 512;     // value dims: the leading part of the latent row

@@ -69,7 +69,8 @@ def test_random_rows_with_gaps_and_tail():
     _check(q, kv, ids, scale, o, lse)
 
 
-@pytest.mark.parametrize("k,seed", [(1, 2), (31, 3), (32, 4), (2048, 5)])
+@pytest.mark.parametrize("k,seed", [(1, 2), (31, 3), (32, 4), (33, 11), (63, 12), (64, 13), (65, 14), (127, 15),
+                                    (2048, 5)])
 def test_topk_widths(k, seed):
     T, Tkv = 9, 5000
     q, kv = W.draw_attention(T, Tkv, seed=seed)
@@ -77,6 +78,29 @@ def test_topk_widths(k, seed):
     scale = 0.06
     o, lse = _gpu(q, kv, ids, scale)
     _check(q, kv, ids, scale, o, lse)
+
+
+def test_one_key_half_empty():
+    # ids are handled in tiles of 64, each half scored by another wave: a half with no valid id
+    # (the other half full) and the reverse, in the same rows
+    T, Tkv, k = 6, 4000, 192
+    q, kv = W.draw_attention(T, Tkv, seed=16)
+    ids = _ids(T, Tkv, k, 16)
+    ids[0::2, 0:32] = -1
+    ids[1::2, 96:128] = -1
+    ids[:, 160:] = -1
+    o, lse = _gpu(q, kv, ids, 0.05)
+    _check(q, kv, ids, 0.05, o, lse)
+
+
+def test_reference_maximum_moves():
+    # scale 1 on unit-variance rows: scores spread over hundreds of units, so a head's running
+    # maximum grows past the slack between tiles many times (the O rescale path)
+    T, Tkv, k = 5, 6000, 1024
+    q, kv = W.draw_attention(T, Tkv, seed=17)
+    ids = _ids(T, Tkv, k, 17)
+    o, lse = _gpu(q, kv, ids, 1.0)
+    _check(q, kv, ids, 1.0, o, lse)
 
 
 def test_single_valid_id_exact():
