@@ -322,34 +322,42 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
     // this stage are free for the P exchange
     *reinterpret_cast<bf16x8*>(kb + xown) = pa0;
     *reinterpret_cast<bf16x8*>(kb + xown + 16) = pa1;
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm);
-    asm volatile("s_barrier" ::: "memory");
-    const bf16x8 qa0 = *reinterpret_cast<const bf16x8*>(kb + xpar);
-    const bf16x8 qa1 = *reinterpret_cast<const bf16x8*>(kb + xpar + 16);
     rescale(alpha);
-    // P of key half 0 then key half 1 (keys ascending), K steps of 16 keys
-    const bf16x8 pk[4] = {kh == 0 ? pa0 : qa0, kh == 0 ? pa1 : qa1, kh == 0 ? qa0 : pa0, kh == 0 ? qa1 : pa1};
+    // The value product over this wave's own keys needs only its own P: its MFMAs are issued
+    // before the pair meets, so the matrix unit works through the barrier and the read of the
+    // partner's P.  Each value block sums this wave's keys first, then the partner's: a fixed
+    // order in every wave.
     auto vread = [&](int nb, int j) __attribute__((always_inline)) {
       const int o1 = trv1[nb & 1] + (nb >> 1) * 128 + 16 * j * kRowBytes;
       const int o2 = trv2[nb & 1] + (nb >> 1) * 128 + 16 * j * kRowBytes;
       return lds_tr_pair(kb + o1, kb + o2);
     };
-    bf16x8 va[4], vn[4];
+    // key half `kc` of every value block: K steps 2*kc and 2*kc + 1
+    auto half_product = [&](int kc, const bf16x8& a0, const bf16x8& a1, f32x16 (&acc)[kDvBlocks])
+        __attribute__((always_inline)) {
+      bf16x8 va[2], vn[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) va[j] = vread(0, j);
+      for (int j = 0; j < 2; ++j) va[j] = vread(0, 2 * kc + j);
 #pragma unroll
-    for (int nb = 0; nb < kDvBlocks; ++nb) {
-      if (nb + 1 < kDvBlocks) {
+      for (int nb = 0; nb < kDvBlocks; ++nb) {
+        if (nb + 1 < kDvBlocks) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) vn[j] = vread(nb + 1, j);
+          for (int j = 0; j < 2; ++j) vn[j] = vread(nb + 1, 2 * kc + j);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        acc[nb] = mfma(a0, va[0], acc[nb]);
+        acc[nb] = mfma(a1, va[1], acc[nb]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) va[j] = vn[j];
       }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) oa[nb] = mfma(pk[j], va[j], oa[nb]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) va[j] = vn[j];
-    }
+    };
+    half_product(kh, pa0, pa1, oa);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+    asm volatile("s_barrier" ::: "memory");
+    const bf16x8 qa0 = *reinterpret_cast<const bf16x8*>(kb + xpar);
+    const bf16x8 qa1 = *reinterpret_cast<const bf16x8*>(kb + xpar + 16);
+    half_product(1 - kh, qa0, qa1, oa);
   };
   if (ntile > 0) gather(stage<0>(), 0);
   for (int kt = 0; kt < ntile; kt += 2) {
