@@ -147,26 +147,36 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
   const int ntile = (p.topk + kAttnTile - 1) / kAttnTile;
   int* const ids = g_ids;
 
-  // the row's ids into LDS (padding past topk = -1); ids outside [-1, Tkv) are flagged and skipped
-  {
-    int bad = 0;
-    for (int j = tid; j < ntile * kAttnTile; j += kAttnThreads) {
-      int id = j < p.topk ? p.ids[t * p.topk + j] : -1;
-      if (id < -1 || id >= p.Tkv) {
-        bad = 1;
-        id = -1;
-      }
-      ids[j] = id;
-    }
-    if (bad) atomicOr(p.ctrl + kCtrlStatus, kStatusBadIds);
+  // The row's ids (at most 8 per thread) and this wave's Q block are loaded with all requests
+  // in flight at once, then the ids go to LDS (padding past topk = -1; ids outside [-1, Tkv)
+  // are flagged and skipped).
+  constexpr int kIdRounds = kMaxTopk / kAttnThreads;
+  int idr[kIdRounds];
+#pragma unroll
+  for (int k = 0; k < kIdRounds; ++k) {
+    const int j = tid + k * kAttnThreads;
+    idr[k] = j < p.topk ? p.ids[t * p.topk + j] : -1;
   }
-
   // B operand of S^T = K . Q^T: column = head h0 + n, K elements = dims 16*st + 8*hf .. +7
   bf16x8 qf[kQkSteps];
   {
     const uint16_t* qrow = p.q + ((t * kAttnHeads + h0 + n) * kAttnDqk) + 8 * hf;
 #pragma unroll
     for (int st = 0; st < kQkSteps; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 16 * st);
+  }
+  {
+    int bad = 0;
+#pragma unroll
+    for (int k = 0; k < kIdRounds; ++k) {
+      const int j = tid + k * kAttnThreads;
+      int id = idr[k];
+      if (id < -1 || id >= p.Tkv) {
+        bad = 1;
+        id = -1;
+      }
+      if (j < ntile * kAttnTile) ids[j] = id;
+    }
+    if (bad) atomicOr(p.ctrl + kCtrlStatus, kStatusBadIds);
   }
   const float c2 = p.scale * kLog2e;   // scores in the exp2 domain
   __syncthreads();
