@@ -34,6 +34,7 @@
 #include <type_traits>
 
 #include "dsa_internal.h"
+#include "wave_ops.h"
 
 namespace dsa {
 namespace {
@@ -127,15 +128,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
   const int n = lane & 31, hf = lane >> 5;
   // Block -> (row, head half), XCD-aware: blocks are dealt to the 8 XCDs round robin, so block
   // b runs on XCD b % 8.  Both halves of a row (which gather the same rows) run on one XCD, and
-  // each XCD takes a contiguous range of rows, whose selections overlap, so the rows running
-  // together on one XCD share its L2.
+  // XCD x takes the rows x, x + 8, x + 16, ...: neighbouring rows' selections overlap, so they
+  // share the XCD's L2, and every XCD gets the same mix of long and short rows (a row of n
+  // valid ids takes ceil(n / 64) tiles).
   int64_t t;
   int half;
   {
     const int64_t b = blockIdx.x, per = (int64_t)p.T / kXcds;
     if (b < 2 * per * kXcds) {
       const int64_t slot = b / kXcds;
-      t = (b % kXcds) * per + (slot >> 1);
+      t = (slot >> 1) * kXcds + b % kXcds;
       half = (int)(slot & 1);
     } else {   // the rows past the last full round of 8: plain order
       const int64_t r = b - 2 * per * kXcds;
@@ -144,18 +146,20 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
     }
   }
   const int h0 = 64 * half + 32 * hg;   // first head of this wave
-  const int ntile = (p.topk + kAttnTile - 1) / kAttnTile;
   int* const ids = g_ids;
 
-  // The row's ids (at most 8 per thread) and this wave's Q block are loaded with all requests
-  // in flight at once, then the ids go to LDS (padding past topk = -1; ids outside [-1, Tkv)
-  // are flagged and skipped).
-  constexpr int kIdRounds = kMaxTopk / kAttnThreads;
-  int idr[kIdRounds];
+  // The row's ids and this wave's Q block are loaded with all requests in flight at once.  The
+  // valid ids are then packed in their order to the front of the LDS list (ids outside
+  // [-1, Tkv) are flagged and treated as -1), so tiles hold only valid ids except at the tail
+  // (padded with -1) and a row of n valid ids takes ceil(n / 64) tiles: -1 entries (the
+  // padding of rows with fewer visible keys than k) cost nothing.  Wave w packs the entries
+  // 512*w .. +511, lane l the 8 entries from 512*w + 8*l.
+  constexpr int kIdsPerLane = kMaxTopk / kAttnThreads;
+  int idr[kIdsPerLane];
+  {
+    const int j0 = 512 * wv + kIdsPerLane * lane;
 #pragma unroll
-  for (int k = 0; k < kIdRounds; ++k) {
-    const int j = tid + k * kAttnThreads;
-    idr[k] = j < p.topk ? p.ids[t * p.topk + j] : -1;
+    for (int k = 0; k < kIdsPerLane; ++k) idr[k] = j0 + k < p.topk ? p.ids[t * p.topk + j0 + k] : -1;
   }
   // B operand of S^T = K . Q^T: column = head h0 + n, K elements = dims 16*st + 8*hf .. +7
   bf16x8 qf[kQkSteps];
@@ -164,19 +168,36 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
 #pragma unroll
     for (int st = 0; st < kQkSteps; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 16 * st);
   }
+  int ntile;
   {
+    uint32_t cnt = 0;
     int bad = 0;
 #pragma unroll
-    for (int k = 0; k < kIdRounds; ++k) {
-      const int j = tid + k * kAttnThreads;
-      int id = idr[k];
-      if (id < -1 || id >= p.Tkv) {
+    for (int k = 0; k < kIdsPerLane; ++k) {
+      if (idr[k] < -1 || idr[k] >= p.Tkv) {
         bad = 1;
-        id = -1;
+        idr[k] = -1;
       }
-      if (j < ntile * kAttnTile) ids[j] = id;
+      cnt += idr[k] >= 0 ? 1u : 0u;
     }
     if (bad) atomicOr(p.ctrl + kCtrlStatus, kStatusBadIds);
+    const uint32_t incl = wave_incl_scan(cnt);
+    if (lane == 63) g_xchg[wv] = __uint_as_float(incl);   // the wave's count, as bits
+    __syncthreads();
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t c = __float_as_uint(g_xchg[w]);
+      before += w < wv ? c : 0u;
+      total += c;
+    }
+    int pos = (int)(before + incl - cnt);
+#pragma unroll
+    for (int k = 0; k < kIdsPerLane; ++k) {
+      if (idr[k] >= 0) ids[pos++] = idr[k];
+    }
+    ntile = ((int)total + kAttnTile - 1) / kAttnTile;
+    for (int j = (int)total + tid; j < ntile * kAttnTile; j += kAttnThreads) ids[j] = -1;
   }
   const float c2 = p.scale * kLog2e;   // scores in the exp2 domain
   __syncthreads();
