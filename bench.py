@@ -277,7 +277,7 @@ def bench_attention(args):
     q_h, kv_h = W.draw_attention(wl.T, wl.Tkv, seed=2)
     q, kv = q_h.to(dev), kv_h.to(dev)
     scale = 1.0 / math.sqrt(576)
-    ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    ws = torch.empty(ix.sparse_attention_workspace_size(wl.T, wl.topk), dtype=torch.uint8, device=dev)
     ix.workspace_init(ws)
     out = torch.empty((wl.T, 128, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((wl.T, 128), dtype=torch.float32, device=dev)

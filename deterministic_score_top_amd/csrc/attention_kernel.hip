@@ -131,10 +131,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
   // XCD x takes the rows x, x + 8, x + 16, ...: neighbouring rows' selections overlap, so they
   // share the XCD's L2, and every XCD gets the same mix of long and short rows (a row of n
   // valid ids takes ceil(n / 64) tiles).
+  // With a split, consecutive blocks are the parts of one (row, head half).
+  const int part = (int)(blockIdx.x % (unsigned)p.split);
   int64_t t;
   int half;
   {
-    const int64_t b = blockIdx.x, per = (int64_t)p.T / kXcds;
+    const int64_t b = blockIdx.x / p.split, per = (int64_t)p.T / kXcds;
     if (b < 2 * per * kXcds) {
       const int64_t slot = b / kXcds;
       t = (slot >> 1) * kXcds + b % kXcds;
@@ -199,6 +201,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
     ntile = ((int)total + kAttnTile - 1) / kAttnTile;
     for (int j = (int)total + tid; j < ntile * kAttnTile; j += kAttnThreads) ids[j] = -1;
   }
+  // this block's tiles: part `part` of `split` equal ranges (empty when the row is short)
+  const int tper = (ntile + p.split - 1) / p.split;
+  const int kbeg = min(ntile, part * tper), kend = min(ntile, kbeg + tper);
   const float c2 = p.scale * kLog2e;   // scores in the exp2 domain
   __syncthreads();
 
@@ -314,7 +319,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
     unsigned char* const kb = stage<S>();
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vector memory counter 0: tile kt has landed
     asm volatile("s_barrier" ::: "memory");
-    if (kt + 1 < ntile) gather(stage<1 - S>(), kt + 1);
+    if (kt + 1 < kend) gather(stage<1 - S>(), kt + 1);
     f32x16 sp = scores(kb);
 
     // mask, scale and the maximum of each head over this wave's keys
@@ -390,10 +395,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
     const bf16x8 qa1 = *reinterpret_cast<const bf16x8*>(kb + xpar + 16);
     half_product(1 - kh, qa0, qa1, oa);
   };
-  if (ntile > 0) gather(stage<0>(), 0);
-  for (int kt = 0; kt < ntile; kt += 2) {
+  if (kbeg < kend) gather(stage<0>(), kbeg);
+  for (int kt = kbeg; kt < kend; kt += 2) {
     step(Int<0>{}, kt);
-    if (kt + 1 >= ntile) break;
+    if (kt + 1 >= kend) break;
     step(Int<1>{}, kt + 1);
   }
 
@@ -406,6 +411,21 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
   __syncthreads();
   const float lp = g_xchg[partner * 32 + n];
   const float lt = kh == 0 ? lw + lp : lp + lw;
+  if (p.split > 1) {
+    // a part's result: O unnormalised and (reference maximum, l) per head, combined with the
+    // other parts by the merge kernel
+    const int64_t prow = (t * p.split + part) * kAttnHeads;
+    float* const orow = p.part_o + ((prow + h0 + 4 * hf) * kAttnDv) + 256 * kh + n;
+#pragma unroll
+    for (int nb = 0; nb < kDvBlocks; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) orow[(8 * (i >> 2) + (i & 3)) * kAttnDv + 32 * nb] = oa[nb][i];
+    if (hf == 0 && kh == 0) {
+      p.part_ml[(prow + h0 + n) * 2] = m;
+      p.part_ml[(prow + h0 + n) * 2 + 1] = lt;
+    }
+    return;
+  }
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (hf == 0) g_fac[wv * 32 + n] = inv;
   __builtin_amdgcn_s_waitcnt(kWaitLgkm);
@@ -423,14 +443,49 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
     p.lse[t * kAttnHeads + h0 + n] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -__builtin_inff();
 }
 
+// Combine the parts of each (row, head): with M the largest reference maximum of the parts and
+// f_s = 2^(m_s - M) (0 for a part without a valid id), l = sum_s f_s l_s and o = sum_s f_s O_s / l,
+// summed over s = 0, 1, ... in that order; lse = (M + log2 l) ln 2.  One 128-thread block per
+// (row, head), four value dims per thread.
+__global__ __launch_bounds__(128) void attention_merge_kernel(AttnParams p) {
+  const int64_t rh = blockIdx.x;   // row * 128 + head
+  const int64_t t = rh / kAttnHeads, h = rh % kAttnHeads;
+  const int S = p.split;
+  float M = -__builtin_inff();
+  for (int s = 0; s < S; ++s) M = fmaxf(M, p.part_ml[((t * S + s) * kAttnHeads + h) * 2]);
+  float L = 0.f;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) {
+    const int64_t ph = (t * S + s) * kAttnHeads + h;
+    const float ms = p.part_ml[ph * 2];
+    const float f = ms == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+    L += f * p.part_ml[ph * 2 + 1];
+    const f32x4 o = *reinterpret_cast<const f32x4*>(p.part_o + ph * kAttnDv + 4 * threadIdx.x);
+    acc += f * o;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  *reinterpret_cast<f32x4*>(p.out + rh * kAttnDv + 4 * threadIdx.x) = acc * inv;
+  if (threadIdx.x == 0) p.lse[rh] = L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -__builtin_inff();
+}
+
 }  // namespace
 
-size_t attn_smem_bytes(int) { return 0; }   // all LDS is static
+int attn_split(int T, int topk) {
+  const int ntile = (topk + kAttnTile - 1) / kAttnTile;
+  int s = 1;
+  while ((int64_t)2 * T * s < kAttnSplitBlocks && s < kAttnMaxSplit && 2 * s <= ntile) s *= 2;
+  return s;
+}
 
-hipError_t attn_prepare(int) { return hipSuccess; }
+size_t attn_partial_bytes(int T, int topk) {
+  const int s = attn_split(T, topk);
+  if (s == 1) return 0;
+  return (size_t)T * s * kAttnHeads * (kAttnDv + 2) * 4u;
+}
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(attention_kernel, dim3(2 * p.T), dim3(kAttnThreads), 0, s, p);
+  hipLaunchKernelGGL(attention_kernel, dim3(2 * p.T * p.split), dim3(kAttnThreads), 0, s, p);
+  if (p.split > 1) hipLaunchKernelGGL(attention_merge_kernel, dim3(p.T * kAttnHeads), dim3(128), 0, s, p);
   return hipGetLastError();
 }
 

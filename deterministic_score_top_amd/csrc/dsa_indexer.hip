@@ -40,7 +40,6 @@ const DeviceInfo* device_info() {
     int bpc = 0;
     if (dsa::score_occupancy(&bpc, dsa::score_smem_limit()) != hipSuccess || bpc < 1) return;
     if (dsa::bwd_prepare() != hipSuccess) return;
-    if (dsa::attn_prepare(dsa::kMaxTopk) != hipSuccess) return;
     info.score_blocks_per_cu = bpc;
     info.ok = true;
     g_info[dev] = info;
@@ -402,6 +401,11 @@ int dsa_indexer_backward(const dsa_indexer_shape* shape, const void* q, const vo
                                  stream, nullptr);
 }
 
+size_t dsa_indexer_sparse_attention_workspace_size(int32_t total_q, int32_t topk) {
+  if (total_q < 0 || topk < 1 || topk > dsa::kMaxTopk) return 0;
+  return (size_t)dsa::kCtrlBytes + dsa::attn_partial_bytes(total_q, topk);
+}
+
 int dsa_indexer_sparse_attention(int32_t total_q, int32_t total_kv, int32_t topk, const void* q,
                                  const void* kv, const int32_t* ids, float scale, float* out,
                                  float* lse, void* workspace, size_t workspace_bytes,
@@ -413,7 +417,7 @@ int dsa_indexer_sparse_attention(int32_t total_q, int32_t total_kv, int32_t topk
   if (!aligned16(workspace) || (q && !aligned16(q)) || (kv && !aligned16(kv)) || (out && !aligned16(out)) ||
       (lse && !aligned16(lse)) || (ids && !aligned4(ids)))
     return DSA_ERR_ALIGN;
-  if (workspace_bytes < (size_t)dsa::kCtrlBytes) return DSA_ERR_WORKSPACE;
+  if (workspace_bytes < dsa_indexer_sparse_attention_workspace_size(total_q, topk)) return DSA_ERR_WORKSPACE;
   if (!device_info()) return DSA_ERR_DEVICE;
   if (total_q == 0) return DSA_OK;
   dsa::AttnParams p;
@@ -426,7 +430,13 @@ int dsa_indexer_sparse_attention(int32_t total_q, int32_t total_kv, int32_t topk
   p.T = total_q;
   p.Tkv = total_kv;
   p.topk = topk;
+  p.split = dsa::attn_split(total_q, topk);
   p.scale = scale;
+  unsigned char* const part = static_cast<unsigned char*>(workspace) + dsa::kCtrlBytes;
+  p.part_o = p.split > 1 ? reinterpret_cast<float*>(part) : nullptr;
+  p.part_ml = p.split > 1 ? reinterpret_cast<float*>(part + (size_t)total_q * p.split * dsa::kAttnHeads *
+                                                                dsa::kAttnDv * 4u)
+                          : nullptr;
   if (dsa::launch_attention(p, stream) != hipSuccess) return DSA_ERR_LAUNCH;
   return DSA_OK;
 }

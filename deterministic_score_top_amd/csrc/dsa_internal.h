@@ -110,6 +110,9 @@ constexpr int kAttnDqk = 576;    // latent row (key) dims
 constexpr int kAttnDv = 512;     // value dims: the leading part of the latent row
 constexpr uint32_t kStatusBadIds = 0x8u;
 
+constexpr int kAttnSplitBlocks = 512;   // a batch with fewer blocks splits its rows' ids
+constexpr int kAttnMaxSplit = 32;
+
 struct AttnParams {
   const uint16_t* q;   // bf16 [T, 128, 576]
   const uint16_t* kv;  // bf16 [Tkv, 576]
@@ -117,11 +120,15 @@ struct AttnParams {
   float* out;          // fp32 [T, 128, 512]
   float* lse;          // fp32 [T, 128]
   uint32_t* ctrl;
-  int32_t T, Tkv, topk;
+  float* part_o;       // split > 1: fp32 [T, split, 128, 512] unnormalised partial outputs
+  float* part_ml;      // split > 1: fp32 [T, split, 128, 2] reference maximum (exp2 domain) and sum
+  int32_t T, Tkv, topk, split;
   float scale;
 };
-size_t attn_smem_bytes(int topk);
-hipError_t attn_prepare(int max_topk);
+// Number of parts each row's ids are split into (a function of the row count and topk only).
+int attn_split(int T, int topk);
+// Workspace bytes past the control block for the partial results (0 when split == 1).
+size_t attn_partial_bytes(int T, int topk);
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
 
 // Dynamic LDS bytes of the score kernel for a tile table of `max_tiles` entries.

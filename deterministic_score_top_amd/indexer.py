@@ -44,6 +44,7 @@ EXPORTED_SYMBOLS = (
     "dsa_indexer_backward",
     "dsa_indexer_backward_ex",
     "dsa_indexer_sparse_attention",
+    "dsa_indexer_sparse_attention_workspace_size",
 )
 STATUS_BAD_IDS = 0x8
 ATTN_HEADS, ATTN_QK_DIM, ATTN_V_DIM = 128, 576, 512
@@ -114,6 +115,8 @@ def lib():
         L.dsa_indexer_backward_ex.restype = ctypes.c_int
         L.dsa_indexer_sparse_attention.argtypes = [i32, i32, i32, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
         L.dsa_indexer_sparse_attention.restype = ctypes.c_int
+        L.dsa_indexer_sparse_attention_workspace_size.argtypes = [i32, i32]
+        L.dsa_indexer_sparse_attention_workspace_size.restype = sz
         _LIB = L
     return _LIB
 
@@ -332,6 +335,14 @@ def backward(q, k, w, cu_seqlens_q, cu_seqlens_k, grad, q_pos_offsets=None, max_
     return dq, dk, dw
 
 
+def sparse_attention_workspace_size(total_q: int, topk: int) -> int:
+    """Workspace bytes dsa_indexer_sparse_attention needs for total_q rows of topk ids."""
+    n = lib().dsa_indexer_sparse_attention_workspace_size(int(total_q), int(topk))
+    if n == 0:
+        raise ValueError(f"unsupported topk {topk}")
+    return n
+
+
 def sparse_attention(q, kv, ids, scale: float, out: Optional[torch.Tensor] = None,
                      lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """Attention of each query row over its selected ids: out fp32 [T, 128, 512], lse fp32 [T, 128].
@@ -355,7 +366,7 @@ def sparse_attention(q, kv, ids, scale: float, out: Optional[torch.Tensor] = Non
     _require(out, "out", torch.float32, (T, ATTN_HEADS, ATTN_V_DIM), dev)
     _require(lse, "lse", torch.float32, (T, ATTN_HEADS), dev)
     if workspace is None:
-        workspace = torch.empty(256, dtype=torch.uint8, device=dev)
+        workspace = torch.empty(sparse_attention_workspace_size(T, k), dtype=torch.uint8, device=dev)
         workspace_init(workspace)
     rc = lib().dsa_indexer_sparse_attention(int(T), int(Tkv), int(k), _ptr(q), _ptr(kv), _ptr(ids), float(scale),
                                             _ptr(out), _ptr(lse), _ptr(workspace),

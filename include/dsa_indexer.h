@@ -182,14 +182,23 @@ int dsa_indexer_backward(const dsa_indexer_shape* shape, const void* q, const vo
  *   ids        int32 [total_q, topk], 1 <= topk <= 2048 (e.g. out_ids of dsa_indexer_topk);
  *              an id outside [-1, total_kv) is skipped and raises DSA_STATUS_BAD_IDS
  *   out        fp32 [total_q, 128, 512], lse fp32 [total_q, 128]: fully overwritten
- *   workspace  the 256-byte control block (dsa_indexer_workspace_init), for the status word
+ *   workspace  dsa_indexer_sparse_attention_workspace_size(total_q, topk) bytes, 16-byte
+ *              aligned, whose first 256 bytes are the control block (dsa_indexer_workspace_init)
+ *              for the status word; a smaller workspace returns DSA_ERR_WORKSPACE
  * Scores are FP32 products of BF16 operands; the softmax runs in FP32 in the exp2 domain and
  * the probabilities are rounded to BF16 for the value product (FP32 accumulation).  Every sum
  * has a fixed order: results are bit-reproducible.  total_kv * 1152 must fit in 31 bits.
+ * A batch with few rows (fewer than 256) splits each row's ids over up to 32 blocks, which
+ * write partial results (unnormalised output, reference maximum and sum per head) to the
+ * workspace; a second dispatch combines the parts in a fixed order.  The split count is a
+ * function of total_q and topk only: the bits of a row do not depend on the other rows' ids
+ * but may differ in rounding between batch sizes with different split counts.
  */
 #define DSA_ATTN_HEADS 128
 #define DSA_ATTN_QK_DIM 576
 #define DSA_ATTN_V_DIM 512
+/* Workspace bytes for dsa_indexer_sparse_attention (0 for an unsupported topk). */
+size_t dsa_indexer_sparse_attention_workspace_size(int32_t total_q, int32_t topk);
 int dsa_indexer_sparse_attention(int32_t total_q, int32_t total_kv, int32_t topk, const void* q,
                                  const void* kv, const int32_t* ids, float scale, float* out,
                                  float* lse, void* workspace, size_t workspace_bytes,

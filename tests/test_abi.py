@@ -161,3 +161,20 @@ def test_sparse_attention_argument_errors():
     assert call(out_=0x40004) == -2 and call(ids_=0x30002) == -2
     assert call(wsb=100) == -4
     assert call(T=0, q_=None, ids_=None, out_=None, lse_=None) in (0, -6)
+
+
+def test_sparse_attention_workspace_size():
+    # few rows split their ids over blocks whose partial results (512 output floats and a
+    # (maximum, sum) pair per head) live past the 256-byte control block
+    L = ix.lib()
+    per_part = 128 * (512 + 2) * 4
+    assert L.dsa_indexer_sparse_attention_workspace_size(256, 2048) == 256   # 512 blocks: no split
+    assert L.dsa_indexer_sparse_attention_workspace_size(4, 2048) == 256 + 4 * 32 * per_part
+    assert L.dsa_indexer_sparse_attention_workspace_size(100, 300) == 256 + 100 * 4 * per_part
+    assert L.dsa_indexer_sparse_attention_workspace_size(4, 64) == 256       # one tile: nothing to split
+    assert L.dsa_indexer_sparse_attention_workspace_size(4, 0) == 0
+    assert L.dsa_indexer_sparse_attention_workspace_size(4, 2049) == 0
+    V = ctypes.c_void_p
+    rc = L.dsa_indexer_sparse_attention(4, 100, 2048, V(0x10000), V(0x20000), V(0x30000), 0.1, V(0x40000),
+                                        V(0x50000), V(0x60000), 256, None)
+    assert rc == -4

@@ -145,7 +145,7 @@ def test_bad_ids_flagged_and_skipped():
     bad = ids.copy()
     bad[1, 3] = Tkv + 7
     bad[2, 0] = -5
-    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(ix.sparse_attention_workspace_size(T, 40), dtype=torch.uint8, device="cuda")
     ix.workspace_init(ws)
     o, lse = _gpu(q, kv, bad, 0.05, workspace=ws)
     status, _, _ = ix.read_status(ws)
@@ -153,6 +153,34 @@ def test_bad_ids_flagged_and_skipped():
     ref = bad.copy()
     ref[(ref < 0) | (ref >= Tkv)] = -1
     _check(q, kv, ref, 0.05, o, lse)
+
+
+@pytest.mark.parametrize("T,k,seed", [(1, 2048, 20), (4, 2048, 21), (3, 700, 22), (17, 1024, 23), (100, 300, 24)])
+def test_few_rows_split_over_blocks(T, k, seed):
+    # fewer than 256 rows: each row's ids are split over several blocks and the partial results
+    # merged; short rows leave some parts without a valid id
+    Tkv = 50000
+    q, kv = W.draw_attention(T, Tkv, seed=seed)
+    ids = _ids(T, Tkv, k, seed, minus=0.3)
+    ids[0, 100:] = -1                     # a short row: most parts are empty
+    if T > 2:
+        ids[2, :] = -1                    # a row without a valid id
+    assert ix.sparse_attention_workspace_size(T, k) > 256
+    o, lse = _gpu(q, kv, ids, 0.05)
+    _check(q, kv, ids, 0.05, o, lse)
+    o2, lse2 = _gpu(q, kv, ids, 0.05)
+    assert np.array_equal(o.view(np.uint32), o2.view(np.uint32))
+    assert np.array_equal(lse.view(np.uint32), lse2.view(np.uint32))
+
+
+def test_split_workspace_too_small_is_rejected():
+    T, Tkv, k = 4, 1000, 512
+    q, kv = W.draw_attention(T, Tkv, seed=25)
+    ids = _ids(T, Tkv, k, 25)
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    ix.workspace_init(ws)
+    with pytest.raises(RuntimeError):
+        _gpu(q, kv, ids, 0.05, workspace=ws)
 
 
 def test_bitwise_reproducible():
