@@ -25,25 +25,26 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense BF16 MFMA
 FLOP_PER_PAIR = 2 * 64 * 128   # one 64x128 by 128x1 contraction per visible (query, key) pair
-SCORE_SRC = os.path.join(ROOT, "deterministic_score_top_amd", "csrc", "score_kernel.hip")
 COPY_BYTES = 512 << 20         # plain copy used to calibrate the FETCH_SIZE / WRITE_SIZE counters
+CSRC = os.path.join(ROOT, "deterministic_score_top_amd", "csrc")
+KERNEL_SRC = {"score": os.path.join(CSRC, "score_kernel.hip"), "attention": os.path.join(CSRC, "attention_kernel.hip")}
 
 
-def score_kernel_hash():
-    return hashlib.sha256(open(SCORE_SRC, "rb").read()).hexdigest()[:16]
+def kernel_hash(kernel="score"):
+    return hashlib.sha256(open(KERNEL_SRC[kernel], "rb").read()).hexdigest()[:16]
 
 
-def traffic_file(config):
-    return os.path.join(ROOT, "profiles", f"score_kernel_traffic_{config}.json")
+def traffic_file(config, kernel="score"):
+    return os.path.join(ROOT, "profiles", f"{kernel}_kernel_traffic_{config}.json")
 
 
-def load_traffic(config):
-    """HBM bytes per score-kernel launch from committed counter runs, if the kernel is unchanged."""
+def load_traffic(config, kernel="score"):
+    """HBM bytes per launch of a kernel from committed counter runs, if its source is unchanged."""
     try:
-        rec = json.load(open(traffic_file(config)))
+        rec = json.load(open(traffic_file(config, kernel)))
     except (OSError, ValueError):
         return None
-    if rec.get("score_kernel_sha256_16") != score_kernel_hash():
+    if rec.get(f"{kernel}_kernel_sha256_16") != kernel_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -59,20 +60,21 @@ def _pmc_avg(run_dir, counter, kernel_substr):
     return sum(vals) / len(vals)
 
 
-def ingest_traffic(config, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
-    """Write profiles/score_kernel_traffic_<config>.json from four rocprofv3 --pmc runs."""
+def ingest_traffic(config, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, kernel="score"):
+    """Write profiles/<kernel>_kernel_traffic_<config>.json from four rocprofv3 --pmc runs."""
     copy_kernel = "copy"
     f_copy = _pmc_avg(copy_fetch_dir, "FETCH_SIZE", copy_kernel)   # KiB per dispatch
     w_copy = _pmc_avg(copy_write_dir, "WRITE_SIZE", copy_kernel)
     f_scale = COPY_BYTES / (f_copy * 1024.0)     # true bytes per counted byte
     w_scale = COPY_BYTES / (w_copy * 1024.0)
-    f = _pmc_avg(fetch_dir, "FETCH_SIZE", "score_kernel") * 1024.0 * f_scale
-    w = _pmc_avg(write_dir, "WRITE_SIZE", "score_kernel") * 1024.0 * w_scale
-    rec = {"config": config, "score_kernel_sha256_16": score_kernel_hash(),
+    name = f"{kernel}_kernel("                   # the kernel itself, not e.g. attention_merge_kernel
+    f = _pmc_avg(fetch_dir, "FETCH_SIZE", name) * 1024.0 * f_scale
+    w = _pmc_avg(write_dir, "WRITE_SIZE", name) * 1024.0 * w_scale
+    rec = {"config": config, f"{kernel}_kernel_sha256_16": kernel_hash(kernel),
            "fetch_bytes_per_launch": f, "write_bytes_per_launch": w, "bytes_per_launch": f + w,
            "copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": f_copy, "write_kib": w_copy,
                                 "fetch_scale": f_scale, "write_scale": w_scale}}
-    json.dump(rec, open(traffic_file(config), "w"), indent=1)
+    json.dump(rec, open(traffic_file(config, kernel), "w"), indent=1)
     print(json.dumps(rec))
 
 
@@ -319,7 +321,8 @@ def bench_attention(args):
         "kernel_ms": k_ms,
         "roofline": {"bound": "mfma", "kernel": "attention_kernel", "achieved": eff, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": eff / PEAK_BF16_TFLOPS, "flop_per_valid_id": ATTN_FLOP_PER_ID,
-                     "gather_bytes_per_valid_id": 2 * 1152, "traffic": None},
+                     "gather_bytes_per_valid_id": 2 * 1152,
+                     "traffic": load_traffic(args.config, "attention")},
     }
     if not args.no_cpu_baseline:
         from oracle import dsa_oracle as O
@@ -368,7 +371,7 @@ def main():
                     help="write the score-kernel traffic record from rocprofv3 --pmc output directories")
     args = ap.parse_args()
     if args.ingest_pmc:
-        ingest_traffic(args.config, *args.ingest_pmc)
+        ingest_traffic(args.config, *args.ingest_pmc, kernel="attention" if args.attention else "score")
         return
     if args.copy_calibration:
         copy_calibration()
