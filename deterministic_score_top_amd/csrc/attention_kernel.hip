@@ -451,17 +451,32 @@ __global__ __launch_bounds__(128) void attention_merge_kernel(AttnParams p) {
   const int64_t rh = blockIdx.x;   // row * 128 + head
   const int64_t t = rh / kAttnHeads, h = rh % kAttnHeads;
   const int S = p.split;
+  // the loops run over the largest split count with the parts past S switched off, so every
+  // part's loads are in flight together; the sums still run s = 0, 1, ... in order
+  float ms[kAttnMaxSplit], ls[kAttnMaxSplit];
+  f32x4 os[kAttnMaxSplit];
+#pragma unroll
+  for (int s = 0; s < kAttnMaxSplit; ++s) {
+    if (s < S) {
+      const int64_t ph = (t * S + s) * kAttnHeads + h;
+      ms[s] = p.part_ml[ph * 2];
+      ls[s] = p.part_ml[ph * 2 + 1];
+      os[s] = *reinterpret_cast<const f32x4*>(p.part_o + ph * kAttnDv + 4 * threadIdx.x);
+    }
+  }
   float M = -__builtin_inff();
-  for (int s = 0; s < S; ++s) M = fmaxf(M, p.part_ml[((t * S + s) * kAttnHeads + h) * 2]);
+#pragma unroll
+  for (int s = 0; s < kAttnMaxSplit; ++s)
+    if (s < S) M = fmaxf(M, ms[s]);
   float L = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < S; ++s) {
-    const int64_t ph = (t * S + s) * kAttnHeads + h;
-    const float ms = p.part_ml[ph * 2];
-    const float f = ms == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-    L += f * p.part_ml[ph * 2 + 1];
-    const f32x4 o = *reinterpret_cast<const f32x4*>(p.part_o + ph * kAttnDv + 4 * threadIdx.x);
-    acc += f * o;
+#pragma unroll
+  for (int s = 0; s < kAttnMaxSplit; ++s) {
+    if (s < S) {
+      const float f = ms[s] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(ms[s] - M);
+      L += f * ls[s];
+      acc += f * os[s];
+    }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   *reinterpret_cast<f32x4*>(p.out + rh * kAttnDv + 4 * threadIdx.x) = acc * inv;

@@ -111,7 +111,7 @@ constexpr int kAttnDv = 512;     // value dims: the leading part of the latent r
 constexpr uint32_t kStatusBadIds = 0x8u;
 
 constexpr int kAttnSplitBlocks = 512;   // a batch with fewer blocks splits its rows' ids
-constexpr int kAttnMaxSplit = 32;
+constexpr int kAttnMaxSplit = 16;
 
 struct AttnParams {
   const uint16_t* q;   // bf16 [T, 128, 576]

@@ -188,7 +188,7 @@ int dsa_indexer_backward(const dsa_indexer_shape* shape, const void* q, const vo
  * Scores are FP32 products of BF16 operands; the softmax runs in FP32 in the exp2 domain and
  * the probabilities are rounded to BF16 for the value product (FP32 accumulation).  Every sum
  * has a fixed order: results are bit-reproducible.  total_kv * 1152 must fit in 31 bits.
- * A batch with few rows (fewer than 256) splits each row's ids over up to 32 blocks, which
+ * A batch with few rows (fewer than 256) splits each row's ids over up to 16 blocks, which
  * write partial results (unnormalised output, reference maximum and sum per head) to the
  * workspace; a second dispatch combines the parts in a fixed order.  The split count is a
  * function of total_q and topk only: the bits of a row do not depend on the other rows' ids

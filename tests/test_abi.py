@@ -169,7 +169,7 @@ def test_sparse_attention_workspace_size():
     L = ix.lib()
     per_part = 128 * (512 + 2) * 4
     assert L.dsa_indexer_sparse_attention_workspace_size(256, 2048) == 256   # 512 blocks: no split
-    assert L.dsa_indexer_sparse_attention_workspace_size(4, 2048) == 256 + 4 * 32 * per_part
+    assert L.dsa_indexer_sparse_attention_workspace_size(4, 2048) == 256 + 4 * 16 * per_part
     assert L.dsa_indexer_sparse_attention_workspace_size(100, 300) == 256 + 100 * 4 * per_part
     assert L.dsa_indexer_sparse_attention_workspace_size(4, 64) == 256       # one tile: nothing to split
     assert L.dsa_indexer_sparse_attention_workspace_size(4, 0) == 0
