@@ -191,3 +191,24 @@ def test_bitwise_reproducible():
     b = _gpu(q, kv, ids, 0.04)
     for x, y in zip(a, b):
         assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+@pytest.mark.parametrize("name,rows", [("causal_n8192", 12), ("zigzag16", 12), ("split_tail", None)])
+def test_full_workload_ids_from_topk(name, rows):
+    # full-size workloads in the configuration bench.py times: the ids are the indexer's top-k of
+    # the workload, the attention runs over every row, seeded sampled rows (every row of the split
+    # tail, whose 4 rows are split over blocks) are checked against the oracle
+    wl = W.make(name)
+    d = "cuda"
+    offs = None if wl.q_pos_offsets is None else wl.q_pos_offsets.to(d)
+    ids, _ = ix.topk(wl.q.to(d), wl.k.to(d), wl.w.to(d), wl.cu_seqlens_q.to(d), wl.cu_seqlens_k.to(d), offs,
+                     topk=wl.topk, max_seqlen_k=wl.max_seqlen_k)
+    q, kv = W.draw_attention(wl.T, wl.Tkv, seed=2)
+    scale = 1.0 / math.sqrt(576)
+    o, lse = ix.sparse_attention(q.to(d), kv.to(d), ids, scale)
+    torch.cuda.synchronize()
+    ids_h = ids.cpu().numpy()
+    sel = np.arange(wl.T) if rows is None else np.sort(np.random.default_rng(3).choice(wl.T, rows, replace=False))
+    if rows is not None:
+        sel[0] = 0                       # the shortest row of the first segment
+    _check(q[sel], kv, ids_h[sel], scale, o[sel].cpu().numpy(), lse[sel].cpu().numpy())
