@@ -248,7 +248,7 @@ __device__ void wave_bases(Smem<NT>& sm, uint32_t eq_skip, uint32_t& sel_base, u
 }
 
 template <int NT>
-__global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
+__global__ __launch_bounds__(NT, NT == 256 ? 6 : 1) void select_kernel(SelectParams p) {
   constexpr int NW = NT / 64;
   constexpr int R = Smem<NT>::R;
   __shared__ Smem<NT> sm;
@@ -297,13 +297,29 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
     int32_t* const oid = p.out_ids + (int64_t)t * topk;
     float* const osc = p.out_scores + (int64_t)t * topk;
     if (n <= topk) {  // every visible key is kept; pad the rest
-      for (int j = tid; j < topk; j += NT) {
-        if (j < n) {
-          oid[j] = kb + j;
-          osc[j] = key_value(row[j]);
-        } else {
-          oid[j] = -1;
-          osc[j] = -__builtin_inff();
+      // a thread's row loads are issued four at a time before their stores (two memory round
+      // trips instead of eight; four keeps the kernel within the registers of six row blocks
+      // per CU)
+      constexpr int kCopyPer = (kMaxTopk + NT - 1) / NT;
+      constexpr int kBatch = kCopyPer < 4 ? kCopyPer : 4;
+#pragma unroll
+      for (int i0 = 0; i0 < kCopyPer; i0 += kBatch) {
+        uint32_t kv[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          const int j = tid + (i0 + i) * NT;
+          kv[i] = j < n ? row[j] : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          const int j = tid + (i0 + i) * NT;
+          if (j < n) {
+            oid[j] = kb + j;
+            osc[j] = key_value(kv[i]);
+          } else if (j < topk) {
+            oid[j] = -1;
+            osc[j] = -__builtin_inff();
+          }
         }
       }
       continue;
