@@ -29,6 +29,11 @@
 //     O rescale is rare; the result is the same softmax, a different but fixed rounding.
 //   * P rounded to BF16 is the A operand of O += P . V, whose V operand is read key-major from
 //     the gathered tile by ds_read_b64_tr_b16.
+//   * The valid ids of a row are packed in order to the front of its list first, so -1 entries
+//     (the padding of rows with fewer visible keys than k) take no tiles.
+//   * A batch of few rows splits each row's tiles into equal parts over several blocks; each part
+//     writes its unnormalised O, reference maximum and sum per head, and a second kernel
+//     combines the parts in part order.
 //   * Every sum has a fixed order, so results are bit-reproducible.
 
 #include <type_traits>
