@@ -212,3 +212,29 @@ def test_full_workload_ids_from_topk(name, rows):
     if rows is not None:
         sel[0] = 0                       # the shortest row of the first segment
     _check(q[sel], kv, ids_h[sel], scale, o[sel].cpu().numpy(), lse[sel].cpu().numpy())
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_random_batches(seed):
+    # seeded random batches: row counts on both sides of the few-row split, any topk, scattered
+    # -1 entries, valid prefixes with a -1 tail, duplicate ids, empty rows, zero and large scales
+    rng = np.random.default_rng(100 + seed)
+    for case in range(8):
+        T = int(rng.choice([1, 2, 3, 5, 13, 64, 100, 255, 256, 300]))
+        k = int(rng.integers(1, 2049))
+        Tkv = int(rng.integers(1, 20000))
+        scale = float(rng.choice([0.0, 0.01, 1.0 / 24, 0.3, 1.0]))
+        q, kv = W.draw_attention(T, Tkv, seed=1000 * seed + case)
+        ids = rng.integers(0, Tkv, size=(T, k)).astype(np.int32)
+        mode = case % 4
+        if mode == 1:
+            ids[rng.random(ids.shape) < rng.random()] = -1
+        elif mode == 2:
+            for t in range(T):
+                ids[t, int(rng.integers(0, k + 1)):] = -1
+        elif mode == 3:
+            ids[:, ::3] = ids[:, :1]
+            ids[rng.random(T) < 0.3] = -1
+        o, lse = _gpu(q, kv, ids, scale)
+        sel = np.arange(T) if T <= 12 else np.sort(rng.choice(T, 12, replace=False))
+        _check(q[sel], kv, ids[sel], scale, o[sel], lse[sel])
