@@ -412,6 +412,8 @@ int dsa_indexer_sparse_attention(int32_t total_q, int32_t total_kv, int32_t topk
                                  hipStream_t stream) {
   if (total_q < 0 || total_kv < 0 || topk < 1 || topk > dsa::kMaxTopk) return DSA_ERR_SHAPE;
   if ((int64_t)total_kv * dsa::kAttnDqk * 2 > INT32_MAX) return DSA_ERR_SHAPE;
+  // two blocks per row (times the split count): the grid must fit a 31-bit block count
+  if ((int64_t)total_q * 2 * dsa::attn_split(total_q, topk) > INT32_MAX) return DSA_ERR_SHAPE;
   if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return DSA_ERR_SHAPE;
   if (!workspace || (total_q > 0 && (!q || !ids || !out || !lse)) || (total_kv > 0 && !kv)) return DSA_ERR_NULL;
   if (!aligned16(workspace) || (q && !aligned16(q)) || (kv && !aligned16(kv)) || (out && !aligned16(out)) ||

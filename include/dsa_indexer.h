@@ -187,7 +187,8 @@ int dsa_indexer_backward(const dsa_indexer_shape* shape, const void* q, const vo
  *              for the status word; a smaller workspace returns DSA_ERR_WORKSPACE
  * Scores are FP32 products of BF16 operands; the softmax runs in FP32 in the exp2 domain and
  * the probabilities are rounded to BF16 for the value product (FP32 accumulation).  Every sum
- * has a fixed order: results are bit-reproducible.  total_kv * 1152 must fit in 31 bits.
+ * has a fixed order: results are bit-reproducible.  total_kv * 1152 and 2 * total_q must fit in
+ * 31 bits (DSA_ERR_SHAPE otherwise).
  * A batch with few rows (fewer than 256) splits each row's ids over up to 16 blocks, which
  * write partial results (unnormalised output, reference maximum and sum per head) to the
  * workspace; a second dispatch combines the parts in a fixed order.  The split count is a

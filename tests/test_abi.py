@@ -156,6 +156,7 @@ def test_sparse_attention_argument_errors():
                                               wsb, None)
     assert call(k=0) == -3 and call(k=2049) == -3 and call(T=-1) == -3
     assert call(Tkv=1864136) == -3                 # 1152-byte rows past 31 bits
+    assert call(T=1 << 30) == -3                    # 2 blocks per row past a 31-bit grid
     assert call(scale=float("nan")) == -3
     assert call(ids_=None) == -1 and call(ws_=None) == -1
     assert call(out_=0x40004) == -2 and call(ids_=0x30002) == -2
