@@ -80,7 +80,6 @@ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; 
 __device__ __forceinline__ int clampi(int64_t x, int lo, int hi) {
   return (int)(x < lo ? lo : (x > hi ? hi : x));
 }
-__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 // g where S > 0 (as int32 the bits of a positive float are positive; +0, -0 and negatives are not)
 __device__ __forceinline__ float pass_pos(float s, float g) { return __float_as_int(s) > 0 ? g : 0.f; }
 
