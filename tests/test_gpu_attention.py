@@ -238,3 +238,40 @@ def test_random_batches(seed):
         o, lse = _gpu(q, kv, ids, scale)
         sel = np.arange(T) if T <= 12 else np.sort(rng.choice(T, 12, replace=False))
         _check(q[sel], kv, ids[sel], scale, o[sel], lse[sel])
+
+
+@pytest.mark.parametrize("T", [4, 300])
+def test_graph_capture_replays_match_eager(T):
+    # the call enqueues only its kernels (one, or two when a few-row batch splits its ids and
+    # merges the parts), with no allocation, memset or host sync, so it can be captured; replays
+    # interleaved with eager calls and synchronisation must each match the eager result bit for bit
+    Tkv, k = 3000, 700
+    q, kv = W.draw_attention(T, Tkv, seed=30 + T)
+    ids = _ids(T, Tkv, k, 30 + T, minus=0.2)
+    d = "cuda"
+    qd, kvd, idd = q.to(d), kv.to(d), torch.as_tensor(ids).to(d)
+    ws = torch.empty(ix.sparse_attention_workspace_size(T, k), dtype=torch.uint8, device=d)
+    ix.workspace_init(ws)
+    o = torch.empty((T, 128, DV), dtype=torch.float32, device=d)
+    lse = torch.empty((T, 128), dtype=torch.float32, device=d)
+    kw = dict(out=o, lse=lse, workspace=ws)
+    ix.sparse_attention(qd, kvd, idd, 0.05, **kw)
+    torch.cuda.synchronize()
+    ref = (o.cpu().numpy().copy(), lse.cpu().numpy().copy())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            ix.sparse_attention(qd, kvd, idd, 0.05, **kw)
+    torch.cuda.current_stream().wait_stream(side)
+    for r in range(4):
+        o.fill_(7.0)
+        lse.fill_(7.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(o.cpu().numpy().view(np.uint32), ref[0].view(np.uint32)), r
+        assert np.array_equal(lse.cpu().numpy().view(np.uint32), ref[1].view(np.uint32)), r
+        ix.sparse_attention(qd, kvd, idd, 0.05, **kw)    # eager work between replays
+        torch.cuda.synchronize()
+    _check(q, kv, ids, 0.05, ref[0], ref[1])
