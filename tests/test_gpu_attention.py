@@ -223,7 +223,7 @@ def test_random_batches(seed):
         T = int(rng.choice([1, 2, 3, 5, 13, 64, 100, 255, 256, 300]))
         k = int(rng.integers(1, 2049))
         Tkv = int(rng.integers(1, 20000))
-        scale = float(rng.choice([0.0, 0.01, 1.0 / 24, 0.3, 1.0]))
+        scale = float(rng.choice([0.0, 0.01, 1.0 / 24, 0.3, 1.0, -0.05, -1.0]))
         q, kv = W.draw_attention(T, Tkv, seed=1000 * seed + case)
         ids = rng.integers(0, Tkv, size=(T, k)).astype(np.int32)
         mode = case % 4
