@@ -377,7 +377,7 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
               "(the scan shards by queries; a multi-GPU driver is not part of this library)", file=sys.stderr)
         sys.exit(2)
 
