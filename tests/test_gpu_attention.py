@@ -275,3 +275,19 @@ def test_graph_capture_replays_match_eager(T):
         ix.sparse_attention(qd, kvd, idd, 0.05, **kw)    # eager work between replays
         torch.cuda.synchronize()
     _check(q, kv, ids, 0.05, ref[0], ref[1])
+
+
+def test_empty_kv_table():
+    # no latent rows at all: every id is -1 or out of range (flagged); every row gets o = 0 and
+    # lse = -inf, split (3 rows) or not (300 rows)
+    for T in (3, 300):
+        q, _ = W.draw_attention(T, 1, seed=40)
+        kv = torch.empty((0, 576), dtype=torch.bfloat16)
+        ids = -np.ones((T, 100), np.int32)
+        ids[0, 5] = 0
+        ws = torch.empty(ix.sparse_attention_workspace_size(T, 100), dtype=torch.uint8, device="cuda")
+        ix.workspace_init(ws)
+        o, lse = _gpu(q, kv, ids, 0.05, workspace=ws)
+        assert np.all(o == 0) and np.all(np.isneginf(lse))
+        status, _, _ = ix.read_status(ws)
+        assert status & ix.STATUS_BAD_IDS
