@@ -346,6 +346,57 @@ def bench_attention(args):
     print(json.dumps(line), flush=True)
 
 
+def warm_up(call, calls, min_s):
+    """`calls` untimed calls, then more until at least `min_s` seconds of back-to-back calls have run
+    (a fresh GPU raises its clock over the first few hundred milliseconds of load)."""
+    import torch
+    n = 0
+    t0 = time.perf_counter()
+    while n < calls or time.perf_counter() - t0 < min_s:
+        for _ in range(16):
+            call()
+        n += 16
+        torch.cuda.synchronize()
+    return n, time.perf_counter() - t0
+
+
+def _pct(v, f):
+    v = sorted(v)
+    return v[min(len(v) - 1, int(round(f * (len(v) - 1))))]
+
+
+def score_kernel_gate(dev, min_warm_s, steps=20, config="causal_n16384", gate=0.5):
+    """Score-kernel fraction of the BF16 peak on one causal document of N=16384 (the score phase
+    must reach half of the peak there), measured in the calling process after its own warm-up."""
+    import torch
+    from deterministic_score_top_amd import indexer as ix
+    from deterministic_score_top_amd import workloads as W
+    wl = W.make(config)
+    q, k, w = wl.q.to(dev), wl.k.to(dev), wl.w.to(dev)
+    cq, ck = wl.cu_seqlens_q.to(dev), wl.cu_seqlens_k.to(dev)
+    offs = None if wl.q_pos_offsets is None else wl.q_pos_offsets.to(dev)
+    ws = ix.alloc_workspace(wl.T, wl.Tkv, wl.B, wl.max_seqlen_k, dev)
+    oi = torch.empty((wl.T, wl.topk), dtype=torch.int32, device=dev)
+    osc = torch.empty((wl.T, wl.topk), dtype=torch.float32, device=dev)
+    kw = dict(topk=wl.topk, workspace=ws, max_seqlen_k=wl.max_seqlen_k, out_ids=oi, out_scores=osc)
+    warm_up(lambda: ix.topk(q, k, w, cq, ck, offs, **kw), 5, min_warm_s)
+    prof = ix.Profiler(steps)
+    for _ in range(steps):
+        ix.topk(q, k, w, cq, ck, offs, profiler=prof, **kw)
+    torch.cuda.synchronize()
+    per_score, per_select = prof.read_calls()
+    prof.close()
+    score_ms = sum(per_score) / len(per_score)
+    eff = FLOP_PER_PAIR * visible_pairs(wl) / (score_ms * 1e-3) / 1e12
+    del ws, oi, osc, q, k, w
+    torch.cuda.empty_cache()
+    return {"workload": config, "calls": steps, "score_kernel_ms": score_ms,
+            "score_kernel_ms_p10_p50_p90": [_pct(per_score, f) for f in (0.1, 0.5, 0.9)],
+            "select_kernel_ms": sum(per_select) / len(per_select),
+            "achieved_tflops": eff, "frac": eff / PEAK_BF16_TFLOPS, "gate_frac": gate,
+            "pass": eff / PEAK_BF16_TFLOPS >= gate}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -354,6 +405,10 @@ def main():
     ap.add_argument("--config", default="causal_n8192")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warmup-s", type=float, default=2.0,
+                    help="after the --warmup calls, keep warming up until this many seconds have passed")
+    ap.add_argument("--no-gate", action="store_true",
+                    help="skip the N=16384 score-kernel measurement that the headline run adds")
     ap.add_argument("--hold-cus", type=int, default=0,
                     help="before each timed call, hold this many CUs with a foreign kernel (tests/native "
                          "helper) for --hold-frac of the warm call time")
@@ -405,9 +460,7 @@ def main():
     call = dict(topk=wl.topk, workspace=ws, max_seqlen_k=wl.max_seqlen_k, out_ids=out_ids, out_scores=out_sc)
 
     flush = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev) if args.cold else None
-    for _ in range(args.warmup):
-        ix.topk(q, k, w, cq, ck, offs, **call)
-    torch.cuda.synchronize()
+    warm_calls, warm_s = warm_up(lambda: ix.topk(q, k, w, cq, ck, offs, **call), args.warmup, args.warmup_s)
     hold = None
     if args.hold_cus > 0:
         import ctypes
@@ -439,9 +492,7 @@ def main():
     calls = len(per_score)
     score_ms, select_ms = sum(per_score), sum(per_select)
     per_call = sorted(a + b for a, b in zip(per_score, per_select))
-
-    def pct(v, f):
-        return v[min(len(v) - 1, int(round(f * (len(v) - 1))))]
+    pct = _pct
     st = ix.read_status(ws)
     if st != (0, 0, 0):
         print(f"bench: workspace status {st}", file=sys.stderr)
@@ -477,6 +528,13 @@ def main():
         "frac_bf16_peak_call": eff_call / PEAK_BF16_TFLOPS,
         "score_kernel_ms": score_avg_ms,
         "select_kernel_ms": select_avg_ms,
+        "warmup_calls_run": warm_calls,
+        "warmup_s_run": warm_s,
+        "score_kernel_ms_per_call": {"first5": per_score[:5], "last5": per_score[-5:],
+                                     "p10": pct(per_score, 0.1), "p50": pct(per_score, 0.5),
+                                     "p90": pct(per_score, 0.9)},
+        "select_kernel_ms_per_call": {"p10": pct(per_select, 0.1), "p50": pct(per_select, 0.5),
+                                      "p90": pct(per_select, 0.9)},
         "call_gpu_ms": {"p10": pct(per_call, 0.1), "p50": pct(per_call, 0.5), "p90": pct(per_call, 0.9),
                         "l2": "cold (512 MiB written between calls)" if args.cold else "warm"},
         "foreign_load": ({"held_cus": args.hold_cus, "held_us": hold_us,
@@ -491,6 +549,11 @@ def main():
         ids_h, sc_h = out_ids.cpu().numpy(), out_sc.cpu().numpy()
         line["cpu_baseline"], ok = cpu_baseline(wl, ids_h, sc_h, args.cpu_budget)
         line["parity_sample_ok"] = ok
+    if args.config == "causal_n8192" and not args.no_gate and hold is None and not args.cold:
+        del ws
+        torch.cuda.empty_cache()
+        print("bench: score-kernel gate on causal_n16384", file=sys.stderr, flush=True)
+        line["score_gate_causal_n16384"] = score_kernel_gate(dev, args.warmup_s)
     print(json.dumps(line), flush=True)
 
 

@@ -132,7 +132,7 @@ __device__ __forceinline__ int swzbits(int row) { return ((row & 3) << 2) | ((ro
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ swzbits(row)) << 4); }
 
 // Validates the segment tables (every thread of the block gets the flags): bit 0 = bad tables,
-// bit 1 = a segment longer than Lmax.  Block 0 records them in the status word.
+// bit 1 = a segment longer than Lmax.  Block 0 records them in the control block.
 __device__ int table_flags(const BwdParams& p, int* scratch) {
   const int tid = threadIdx.x;
   if (tid == 0) scratch[10] = 0;
@@ -151,8 +151,13 @@ __device__ int table_flags(const BwdParams& p, int* scratch) {
   if (flags) atomicOr(&scratch[10], flags);
   __syncthreads();
   flags = scratch[10];
-  if (blockIdx.x == 0 && tid == 0 && flags)
-    atomicOr(p.ctrl + kCtrlStatus, ((flags & 1) ? kStatusBadSegments : 0u) | ((flags & 2) ? kStatusSeqlenBound : 0u));
+  if (blockIdx.x == 0 && tid == 0) {
+    // this call's verdict for the reduce kernels that follow (always overwritten); the status
+    // word is sticky and only reports
+    p.ctrl[kCtrlCallBad] = (flags & 1) ? 1u : 0u;
+    if (flags)
+      atomicOr(p.ctrl + kCtrlStatus, ((flags & 1) ? kStatusBadSegments : 0u) | ((flags & 2) ? kStatusSeqlenBound : 0u));
+  }
   return flags;
 }
 
@@ -586,7 +591,7 @@ struct Tree<1> {
 template <int P>
 __global__ __launch_bounds__(256) void bwd_dk_reduce_kernel(const float* __restrict__ part, float* __restrict__ dk,
                                                             int64_t n4, const uint32_t* ctrl) {
-  if (ctrl[kCtrlStatus] & kStatusBadSegments) return;
+  if (ctrl[kCtrlCallBad]) return;  // this call's tables are invalid
   const f32x4* src = reinterpret_cast<const f32x4*>(part);
   f32x4* out = reinterpret_cast<f32x4*>(dk);
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x)
@@ -599,7 +604,7 @@ __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const float* __restr
                                                             const float* __restrict__ part_w,
                                                             const float* __restrict__ w, float* __restrict__ dq,
                                                             float* __restrict__ dw, int64_t T, const uint32_t* ctrl) {
-  if (ctrl[kCtrlStatus] & kStatusBadSegments) return;
+  if (ctrl[kCtrlCallBad]) return;  // this call's tables are invalid
   const int64_t nq4 = T * (kHeads * kDim / 4), nw4 = T * (kHeads / 4);
   const f32x4* sq = reinterpret_cast<const f32x4*>(part_q);
   const f32x4* sw = reinterpret_cast<const f32x4*>(part_w);

@@ -21,6 +21,7 @@ struct DeviceInfo {
   bool ok = false;
   int cus = 0;
   int score_blocks_per_cu = 0;  // at the smem limit (a lower bound for smaller tables)
+  dsa::SelectOccupancy select;  // resident blocks per CU of each select variant
 };
 
 constexpr int kMaxDevices = 64;
@@ -40,6 +41,7 @@ const DeviceInfo* device_info() {
     int bpc = 0;
     if (dsa::score_occupancy(&bpc, dsa::score_smem_limit()) != hipSuccess || bpc < 1) return;
     if (dsa::bwd_prepare() != hipSuccess) return;
+    if (dsa::select_occupancy(&info.select) != hipSuccess) return;
     info.score_blocks_per_cu = bpc;
     info.ok = true;
     g_info[dev] = info;
@@ -50,9 +52,9 @@ const DeviceInfo* device_info() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// Row length bound: max_seqlen_k, or total_k when it is 0 (check_shape keeps both <= 65536).
 int64_t lmax_of(const dsa_indexer_shape* s) {
   int64_t L = s->max_seqlen_k > 0 ? s->max_seqlen_k : s->total_k;
-  if (L > dsa::kMaxSeqlenK) L = dsa::kMaxSeqlenK;
   if (L < 1) L = 1;
   return L;
 }
@@ -66,6 +68,9 @@ int check_shape(const dsa_indexer_shape* s) {
   if (s->num_segments < 1 || s->total_q < 0 || s->total_k < 0) return DSA_ERR_SHAPE;
   if (s->num_heads != dsa::kHeads || s->head_dim != dsa::kDim) return DSA_ERR_SHAPE;
   if (s->max_seqlen_k < 0 || s->max_seqlen_k > dsa::kMaxSeqlenK) return DSA_ERR_SHAPE;
+  // without a stated bound the bound is total_k, which must then be a supported row length
+  // (a longer segment would otherwise be cut without an error)
+  if (s->max_seqlen_k == 0 && s->total_k > dsa::kMaxSeqlenK) return DSA_ERR_SHAPE;
   return DSA_OK;
 }
 
@@ -182,7 +187,8 @@ int dsa_indexer_topk_ex(const dsa_indexer_shape* shape, const void* q, const voi
   if (shape->total_q > 0 && (!out_ids || !out_scores)) return DSA_ERR_NULL;
   if ((out_ids && !aligned16(out_ids)) || (out_scores && !aligned16(out_scores))) return DSA_ERR_ALIGN;
   if (workspace_bytes < dsa_indexer_workspace_size(shape)) return DSA_ERR_WORKSPACE;
-  if (!device_info()) return DSA_ERR_DEVICE;
+  const DeviceInfo* dev = device_info();
+  if (!dev) return DSA_ERR_DEVICE;
   if (profiler && profiler->used >= profiler->capacity) return DSA_ERR_SHAPE;
   if (shape->total_q == 0) return DSA_OK;
 
@@ -211,7 +217,7 @@ int dsa_indexer_topk_ex(const dsa_indexer_shape* shape, const void* q, const voi
   sp.Tkv = shape->total_k;
   sp.Lmax = (int32_t)lmax_of(shape);
   sp.topk = topk;
-  if (dsa::launch_select(sp, stream) != hipSuccess) return DSA_ERR_LAUNCH;
+  if (dsa::launch_select(sp, dev->cus, dev->select, stream) != hipSuccess) return DSA_ERR_LAUNCH;
   if (ev) {
     if (hipEventRecord(ev[2], stream) != hipSuccess) return DSA_ERR_LAUNCH;
     profiler->used++;

@@ -29,6 +29,9 @@ constexpr int kCtrlTicket = 0;
 constexpr int kCtrlDone = 1;
 constexpr int kCtrlStatus = 2;
 constexpr int kCtrlExpected = 3;  // final counter value of the score kernel, for the select kernel's check
+// Verdict of the current call on its segment tables (1 = invalid), overwritten by the first kernel
+// of every call and read by the kernels after it; the status word above is sticky and only reports.
+constexpr int kCtrlCallBad = 4;
 
 constexpr uint32_t kStatusCorruptCounter = 0x1u;
 constexpr uint32_t kStatusBadSegments = 0x2u;
@@ -138,8 +141,13 @@ hipError_t score_prepare(size_t max_smem);
 hipError_t score_occupancy(int* blocks_per_cu, size_t smem);
 hipError_t launch_score(const ScoreParams& p, int grid, size_t smem, hipStream_t s);
 
-// Select kernel variant by the longest row it must hold in registers.
-hipError_t launch_select(const SelectParams& p, hipStream_t s);
+// Resident blocks per CU of the select kernel variants (queried once per device).
+struct SelectOccupancy {
+  int narrow = 1;  // 256-thread rows
+  int wide = 1;    // 1024-thread rows (batches with few rows)
+};
+hipError_t select_occupancy(SelectOccupancy* occ);
+hipError_t launch_select(const SelectParams& p, int cus, const SelectOccupancy& occ, hipStream_t s);
 
 hipError_t launch_ctrl_init(uint32_t* ctrl, hipStream_t s);
 

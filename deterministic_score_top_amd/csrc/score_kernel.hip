@@ -297,6 +297,9 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
     block_scan_excl(unit_pf, ntiles, part);
     units = unit_pf[ntiles];
   }
+  // this call's verdict on its tables, for the select kernel (always overwritten, so a bad call
+  // does not affect later calls on the same workspace)
+  if (blockIdx.x == 0 && tid == 0) p.ctrl[kCtrlCallBad] = (plan_flags & 1) ? 1u : 0u;
   if (tid == 0 && plan_flags) {
     uint32_t st = 0;
     if (plan_flags & 1) st |= kStatusBadSegments;

@@ -254,7 +254,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 6 : 1) void select_kernel(SelectPar
   __shared__ Smem<NT> sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int topk = p.topk;
-  const bool bad = (p.ctrl[kCtrlStatus] & kStatusBadSegments) != 0;
+  const bool bad = p.ctrl[kCtrlCallBad] != 0u;  // this call's tables are invalid: all rows padding
   if (blockIdx.x == 0 && tid == 0) {
     // the score kernel drew units + grid tickets; anything else means the counter was not zero
     // when it started.  Reset for the next call (this kernel runs after the score kernel).
@@ -602,31 +602,29 @@ __global__ __launch_bounds__(NT, NT == 256 ? 6 : 1) void select_kernel(SelectPar
   }
 }
 
-template <int NT>
-hipError_t launch_variant(const SelectParams& p, hipStream_t s) {
-  int dev = 0, cus = 0, bpc = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return hipErrorInvalidDevice;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, select_kernel<NT>, NT, 0) != hipSuccess || bpc < 1)
-    bpc = 1;
-  const int grid = min(p.T, cus * bpc * 4);
-  hipLaunchKernelGGL((select_kernel<NT>), dim3(grid), dim3(NT), 0, s, p);
-  return hipGetLastError();
-}
-
 }  // namespace
 
-hipError_t launch_select(const SelectParams& p, hipStream_t s) {
+hipError_t select_occupancy(SelectOccupancy* occ) {
+  int a = 0, b = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, select_kernel<256>, 256, 0);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, select_kernel<1024>, 1024, 0);
+  if (e != hipSuccess) return e;
+  occ->narrow = a < 1 ? 1 : a;
+  occ->wide = b < 1 ? 1 : b;
+  return hipSuccess;
+}
+
+hipError_t launch_select(const SelectParams& p, int cus, const SelectOccupancy& occ, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return hipErrorInvalidDevice;
   // Few rows (a split tail, a handful of decode queries) leave most CUs idle: give each row
   // 16 waves instead of 4, so its passes over the keys take a quarter of the steps.
-  if (4 * p.T <= cus) return launch_variant<1024>(p, s);
-  return launch_variant<256>(p, s);
+  if (4 * p.T <= cus) {
+    hipLaunchKernelGGL((select_kernel<1024>), dim3(min(p.T, cus * occ.wide * 4)), dim3(1024), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((select_kernel<256>), dim3(min(p.T, cus * occ.narrow * 4)), dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace dsa

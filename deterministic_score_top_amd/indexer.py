@@ -274,7 +274,7 @@ def scores(q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets=None, max_seqlen_k
     Columns past each row's visible count keep whatever `out` held (NaN if allocated here).
     """
     dev, T, Tkv, B = _inputs(q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets)
-    L = max_seqlen_k if max_seqlen_k > 0 else min(max(Tkv, 1), MAX_SEQLEN_K)
+    L = max_seqlen_k if max_seqlen_k > 0 else max(Tkv, 1)
     ld = (L + 3) // 4 * 4
     if out is None:
         out = torch.full((T, ld), float("nan"), dtype=torch.float32, device=dev)

@@ -61,7 +61,10 @@ extern "C" {
 #define DSA_ERR_LAUNCH (-5)     /* a HIP launch failed; re-run dsa_indexer_workspace_init      */
 #define DSA_ERR_DEVICE (-6)     /* current device is not gfx950 or cannot be queried           */
 
-/* Device status bits, left in the workspace control block by the kernels. */
+/* Device status bits, left in the workspace control block by the kernels.  They are sticky
+   (reporting only; cleared by dsa_indexer_workspace_init): whether a call's segment tables are
+   valid is decided again by every call, so a call with invalid tables does not affect later
+   calls on the same workspace. */
 #define DSA_STATUS_CORRUPT_COUNTER 0x1u /* work-unit counter was not zero at entry          */
 #define DSA_STATUS_BAD_SEGMENTS 0x2u    /* cu_seqlens not 0-based, non-decreasing, ending at T/Tkv */
 #define DSA_STATUS_SEQLEN_BOUND 0x4u    /* a segment has more keys than max_seqlen_k; its
@@ -82,7 +85,9 @@ typedef struct dsa_indexer_shape {
   int32_t total_k;      /* Tkv >= 0: rows of k                                                */
   int32_t num_heads;    /* H, must be 64                                                      */
   int32_t head_dim;     /* D, must be 128                                                     */
-  int32_t max_seqlen_k; /* upper bound on any segment's key count, 1..65536; 0 = min(Tkv,65536) */
+  int32_t max_seqlen_k; /* upper bound on any segment's key count, 1..65536; 0 = Tkv, which
+                           must then be <= 65536 (DSA_ERR_SHAPE otherwise: a caller with more
+                           keys states the bound)                                           */
 } dsa_indexer_shape;
 
 /*
@@ -96,8 +101,9 @@ size_t dsa_indexer_workspace_size(const dsa_indexer_shape* shape);
 /*
  * Zero the workspace control block, on `stream` (a small fill kernel, no memset, so the call
  * can be captured in a graph).  Needed once per workspace before its first use, and again
- * after any call that returned DSA_ERR_LAUNCH or left a status bit set.  Every completed call
- * leaves the counters at zero again, so steady-state calls pay no reset.  Initialise and
+ * after any call that returned DSA_ERR_LAUNCH (a kernel that did not run leaves the work-unit
+ * counter where it stopped).  Every completed call leaves the counters at zero again, so
+ * steady-state calls pay no reset; the sticky status bits are cleared only here.  Initialise and
  * call on the same stream, or order the two streams (the page's stream-ordering note for
  * prepared runners).
  */
@@ -106,6 +112,12 @@ int dsa_indexer_workspace_init(void* workspace, size_t workspace_bytes, hipStrea
 /*
  * The scan.  Enqueues the score kernel (persistent grid drawing work units from the
  * self-resetting counter in the workspace) and the per-row top-k select kernel on `stream`.
+ * Two dispatches, not one fused scan program: the score kernel writes every visible score of a
+ * query to a dense row in the workspace (the order-preserving 32-bit key of the FP32 score),
+ * and the select kernel takes each row's exact top-k from it.  This is why the workspace holds
+ * T rows of round_up(max_seqlen_k, 64) words (1 GiB for 16384 queries of 16384 keys) and why a
+ * segment may hold at most 65536 keys; in exchange a query's keys can be split over work units
+ * with no partial lists to merge and no waiting between blocks.
  *   q              bf16 [T, 64, 128]
  *   k              bf16 [Tkv, 128]
  *   w              fp32 [T, 64]

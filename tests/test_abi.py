@@ -8,10 +8,14 @@ import os
 import re
 
 import pytest
+import torch
 
 from deterministic_score_top_amd import indexer as ix
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+# Placeholder addresses are used throughout; a call whose arguments all pass would enqueue work
+# on them, so such calls are made only where no GPU is present (they stop at the device check).
+NO_GPU = not torch.cuda.is_available()
 HEADER = os.path.join(ROOT, "include", "dsa_indexer.h")
 
 
@@ -37,6 +41,12 @@ def test_workspace_size():
         ix.workspace_size(10, 100, 0, 0)
     with pytest.raises(ix.DsaError):
         ix.workspace_size(10, 100, 1, 70000)
+    # no stated bound: the bound is total_k, which must itself be a supported row length (more
+    # than 65536 keys without a bound would cut a long segment without an error)
+    assert ix.workspace_size(10, 65536, 1, 0) == 256 + 10 * 65536 * 4
+    with pytest.raises(ix.DsaError):
+        ix.workspace_size(10, 65537, 3, 0)
+    assert ix.workspace_size(10, 175428, 32, 65536) == 256 + 10 * 65536 * 4
 
 
 def test_status_strings():
@@ -82,6 +92,19 @@ def test_argument_errors():
     assert _call(bad, GOOD) == -3
     bad = ix.make_shape(16, 64, 0, 64)
     assert _call(bad, GOOD) == -3
+    # more than 65536 keys with max_seqlen_k = 0 is rejected before any device work, by every
+    # entry point that takes the shape
+    unbounded = ix.make_shape(16, 70000, 2, 0)
+    assert _call(unbounded, GOOD) == -3
+    if NO_GPU:   # with the bound stated the arguments pass; the call then stops at the device check
+        assert _call(ix.make_shape(16, 70000, 2, 65536), GOOD) == -6
+    L = ix.lib()
+    V = ctypes.c_void_p
+    q, k, w, cq, ck, _, g, dq, ws = GOOD
+    assert L.dsa_indexer_scores(ctypes.byref(unbounded), V(q), V(k), V(w), V(cq), V(ck), None, V(g), 70000,
+                                V(ws), 1 << 40, None) == -3
+    assert L.dsa_indexer_backward(ctypes.byref(unbounded), V(q), V(k), V(w), V(cq), V(ck), None, V(g), 70000,
+                                  V(dq), V(0x90000), V(0xA0000), V(ws), 1 << 40, None) == -3
 
 
 def test_empty_inputs_may_be_null():
@@ -92,8 +115,9 @@ def test_empty_inputs_may_be_null():
     r = _call(no_q, (None, 0x20000, None, 0x40000, 0x50000, None, None, None, 0x80000))
     assert r in (0, -6)
     no_k = ix.make_shape(16, 0, 1, 64)
-    r = _call(no_k, (0x10000, None, 0x30000, 0x40000, 0x50000, None, 0x60000, 0x70000, 0x80000))
-    assert r in (0, -6)
+    if NO_GPU:   # (on a GPU this call would run on the placeholder addresses)
+        r = _call(no_k, (0x10000, None, 0x30000, 0x40000, 0x50000, None, 0x60000, 0x70000, 0x80000))
+        assert r == -6
     s = ix.make_shape(16, 64, 1, 64)
     assert _call(s, _with(1, None)) == -1          # k NULL with keys present
     assert _call(s, _with(6, None)) == -1          # out_ids NULL with queries present
@@ -127,7 +151,7 @@ def test_backward_argument_errors():
     dq_part = 64 * 16 * (64 * 128 + 64) * 4
     assert ix.backward_workspace_size(16, 64, 1) == 256 + 64 * 64 * 128 * 4 + dq_part
     # 175 428 keys: 686 key blocks fill the GPU alone, no dk partials
-    assert ix.backward_workspace_size(16, 175428, 1) == 256 + dq_part
+    assert ix.backward_workspace_size(16, 175428, 1, 65536) == 256 + dq_part
     # 8192 queries and keys: 2048 query tiles, 32 key blocks x 16 parts
     assert ix.backward_workspace_size(8192, 8192, 1) == 256 + 16 * 8192 * 128 * 4
     q, k, w, cq, ck, _, g, dq, ws = GOOD
@@ -143,7 +167,8 @@ def test_backward_argument_errors():
     assert call(ld=66) == -3                     # not a multiple of 4
     assert call(ws_bytes=1000) == -4
     no_k = ix.make_shape(16, 0, 1, 64)
-    assert call(dk_=None, shape=no_k) in (0, -6)  # no keys: dk may be NULL
+    if NO_GPU:   # no keys: dk may be NULL (the call reaches the device check)
+        assert call(dk_=None, shape=no_k) == -6
 
 
 def test_sparse_attention_argument_errors():

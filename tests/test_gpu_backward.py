@@ -248,6 +248,28 @@ def test_bad_tables_leave_outputs_untouched():
         assert np.all(x == 7.0)
 
 
+def test_bad_tables_then_good_tables_same_workspace():
+    # few queries and keys: both reduce kernels run.  After a call with invalid tables the next
+    # call with valid tables on the same workspace (not re-initialised) must give exactly what a
+    # fresh workspace gives: the reduce kernels gate on this call's verdict, not on the sticky
+    # status bit
+    wl = W.random_segments([10, 10], [64, 64], [0, 0], topk=8, seed=45)
+    grad = W.draw_grad(wl.T, _ld(wl), seed=45)
+    d = "cuda"
+    ws = torch.empty(ix.backward_workspace_size(wl.T, wl.Tkv, wl.B), dtype=torch.uint8, device=d)
+    ix.workspace_init(ws)
+    good_q, good_k = wl.cu_seqlens_q, wl.cu_seqlens_k
+    wl.cu_seqlens_k = torch.tensor([0, 64, 100], dtype=torch.int32)   # does not end at Tkv = 128
+    _gpu(wl, grad, workspace=ws)
+    assert ix.read_status(ws)[0] & ix.STATUS_BAD_SEGMENTS
+    wl.cu_seqlens_q, wl.cu_seqlens_k = good_q, good_k
+    got = _gpu(wl, grad, workspace=ws)
+    ref = _gpu(wl, grad)   # fresh workspace
+    for g, r in zip(got, ref):
+        assert np.array_equal(g.view(np.uint32), r.view(np.uint32))
+    assert np.any(got[1] != 0) and np.any(got[0] != 0)
+
+
 def test_causal_n8192_sampled_rows_and_keys():
     wl = W.make("causal_n8192")
     grad = W.draw_grad(wl.T, _ld(wl), seed=44)
