@@ -9,6 +9,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <mutex>
 #include <string.h>
 #include <vector>
@@ -16,6 +17,13 @@
 #include "dsa_internal.h"
 
 namespace {
+
+// Fixed device memory of the entry point that allocates nothing (dsa_indexer_topk_noalloc): a
+// control block and score rows, like a caller's workspace.  Each device the library runs on
+// holds its own copy until the process ends.  In host code `scratch` names a host-side stand-in,
+// not the device copy: kernels and fills take the per-device address from hipGetSymbolAddress.
+constexpr size_t kScratchBytes = (size_t)dsa::kCtrlBytes + ((size_t)64 << 20);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 struct DeviceInfo {
   bool ok = false;
@@ -27,6 +35,20 @@ struct DeviceInfo {
 constexpr int kMaxDevices = 64;
 std::once_flag g_once[kMaxDevices];
 DeviceInfo g_info[kMaxDevices];
+// Per device: the address of its copy of `scratch` (looked up once, with the device current)
+// and whether its control block is known to be zero (cleared by the first no-allocation call on
+// the device, and again after a call that failed to launch).
+std::once_flag g_scratch_once[kMaxDevices];
+unsigned char* g_scratch_ptr[kMaxDevices];
+std::atomic<bool> g_scratch_clean[kMaxDevices];
+
+unsigned char* scratch_of(int dev) {
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* sp = nullptr;
+    if (hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch)) == hipSuccess) g_scratch_ptr[dev] = static_cast<unsigned char*>(sp);
+  });
+  return g_scratch_ptr[dev];
+}
 
 const DeviceInfo* device_info() {
   int dev = 0;
@@ -136,17 +158,33 @@ int launch_scores(const Call& c, hipStream_t stream) {
   return DSA_OK;
 }
 
-int check_common(const dsa_indexer_shape* shape, const void* q, const void* k, const float* w,
-                 const int32_t* cu_q, const int32_t* cu_k, const int32_t* offs,
-                 const void* workspace) {
+int check_inputs(const dsa_indexer_shape* shape, const void* q, const void* k, const float* w,
+                 const int32_t* cu_q, const int32_t* cu_k, const int32_t* offs) {
   int rc = check_shape(shape);
   if (rc) return rc;
   // q and w may be NULL when there are no queries, k when there are no keys
   const bool has_q = shape->total_q > 0, has_k = shape->total_k > 0;
-  if ((has_q && (!q || !w)) || (has_k && !k) || !cu_q || !cu_k || !workspace) return DSA_ERR_NULL;
-  if ((q && !aligned16(q)) || (k && !aligned16(k)) || (w && !aligned16(w)) || !aligned16(workspace))
-    return DSA_ERR_ALIGN;
+  if ((has_q && (!q || !w)) || (has_k && !k) || !cu_q || !cu_k) return DSA_ERR_NULL;
+  if ((q && !aligned16(q)) || (k && !aligned16(k)) || (w && !aligned16(w))) return DSA_ERR_ALIGN;
   if (!aligned4(cu_q) || !aligned4(cu_k) || (offs && !aligned4(offs))) return DSA_ERR_ALIGN;
+  return DSA_OK;
+}
+
+int check_common(const dsa_indexer_shape* shape, const void* q, const void* k, const float* w,
+                 const int32_t* cu_q, const int32_t* cu_k, const int32_t* offs,
+                 const void* workspace) {
+  int rc = check_inputs(shape, q, k, w, cu_q, cu_k, offs);
+  if (rc) return rc;
+  if (!workspace) return DSA_ERR_NULL;
+  if (!aligned16(workspace)) return DSA_ERR_ALIGN;
+  return DSA_OK;
+}
+
+int check_outputs(const dsa_indexer_shape* shape, int32_t topk, const int32_t* out_ids,
+                  const float* out_scores) {
+  if (topk < 1 || topk > dsa::kMaxTopk) return DSA_ERR_SHAPE;
+  if (shape->total_q > 0 && (!out_ids || !out_scores)) return DSA_ERR_NULL;
+  if ((out_ids && !aligned16(out_ids)) || (out_scores && !aligned16(out_scores))) return DSA_ERR_ALIGN;
   return DSA_OK;
 }
 
@@ -157,6 +195,49 @@ struct dsa_indexer_profiler {
   int used = 0;
   std::vector<hipEvent_t> ev;  // 3 per slot: before score, between, after select
 };
+
+namespace {
+
+// The two kernels of the scan on a validated call; `ws` is a control block followed by the
+// score rows (a caller's workspace or this device's scratch).
+int enqueue_topk(const DeviceInfo* dev, const dsa_indexer_shape* shape, const void* q, const void* k,
+                 const float* w, const int32_t* cu_q, const int32_t* cu_k, const int32_t* offs,
+                 int32_t topk, int32_t* out_ids, float* out_scores, unsigned char* ws,
+                 hipStream_t stream, const dsa_indexer_tuning* tuning, dsa_indexer_profiler* profiler) {
+  uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws);
+  float* scores = reinterpret_cast<float*>(ws + dsa::kCtrlBytes);
+  const int64_t ld = row_stride(shape);
+  hipEvent_t* ev = profiler ? &profiler->ev[3 * profiler->used] : nullptr;
+
+  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return DSA_ERR_LAUNCH;
+  Call c{shape, q, k, w, cu_q, cu_k, offs, scores, ld, ctrl, tuning, 1};
+  int rc = launch_scores(c, stream);
+  if (rc) return rc;
+  if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return DSA_ERR_LAUNCH;
+
+  dsa::SelectParams sp;
+  sp.keys = reinterpret_cast<const uint32_t*>(scores);
+  sp.ld = ld;
+  sp.cu_q = cu_q;
+  sp.cu_k = cu_k;
+  sp.offs = offs;
+  sp.out_ids = out_ids;
+  sp.out_scores = out_scores;
+  sp.ctrl = ctrl;
+  sp.B = shape->num_segments;
+  sp.T = shape->total_q;
+  sp.Tkv = shape->total_k;
+  sp.Lmax = (int32_t)lmax_of(shape);
+  sp.topk = topk;
+  if (dsa::launch_select(sp, dev->cus, dev->select, stream) != hipSuccess) return DSA_ERR_LAUNCH;
+  if (ev) {
+    if (hipEventRecord(ev[2], stream) != hipSuccess) return DSA_ERR_LAUNCH;
+    profiler->used++;
+  }
+  return DSA_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -183,46 +264,15 @@ int dsa_indexer_topk_ex(const dsa_indexer_shape* shape, const void* q, const voi
                         dsa_indexer_profiler* profiler) {
   int rc = check_common(shape, q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets, workspace);
   if (rc) return rc;
-  if (topk < 1 || topk > dsa::kMaxTopk) return DSA_ERR_SHAPE;
-  if (shape->total_q > 0 && (!out_ids || !out_scores)) return DSA_ERR_NULL;
-  if ((out_ids && !aligned16(out_ids)) || (out_scores && !aligned16(out_scores))) return DSA_ERR_ALIGN;
+  rc = check_outputs(shape, topk, out_ids, out_scores);
+  if (rc) return rc;
   if (workspace_bytes < dsa_indexer_workspace_size(shape)) return DSA_ERR_WORKSPACE;
   const DeviceInfo* dev = device_info();
   if (!dev) return DSA_ERR_DEVICE;
   if (profiler && profiler->used >= profiler->capacity) return DSA_ERR_SHAPE;
   if (shape->total_q == 0) return DSA_OK;
-
-  uint32_t* ctrl = static_cast<uint32_t*>(workspace);
-  float* scores = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + dsa::kCtrlBytes);
-  const int64_t ld = row_stride(shape);
-  hipEvent_t* ev = profiler ? &profiler->ev[3 * profiler->used] : nullptr;
-
-  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return DSA_ERR_LAUNCH;
-  Call c{shape, q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets, scores, ld, ctrl, tuning, 1};
-  rc = launch_scores(c, stream);
-  if (rc) return rc;
-  if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return DSA_ERR_LAUNCH;
-
-  dsa::SelectParams sp;
-  sp.keys = reinterpret_cast<const uint32_t*>(scores);
-  sp.ld = ld;
-  sp.cu_q = cu_seqlens_q;
-  sp.cu_k = cu_seqlens_k;
-  sp.offs = q_pos_offsets;
-  sp.out_ids = out_ids;
-  sp.out_scores = out_scores;
-  sp.ctrl = ctrl;
-  sp.B = shape->num_segments;
-  sp.T = shape->total_q;
-  sp.Tkv = shape->total_k;
-  sp.Lmax = (int32_t)lmax_of(shape);
-  sp.topk = topk;
-  if (dsa::launch_select(sp, dev->cus, dev->select, stream) != hipSuccess) return DSA_ERR_LAUNCH;
-  if (ev) {
-    if (hipEventRecord(ev[2], stream) != hipSuccess) return DSA_ERR_LAUNCH;
-    profiler->used++;
-  }
-  return DSA_OK;
+  return enqueue_topk(dev, shape, q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets, topk, out_ids,
+                      out_scores, static_cast<unsigned char*>(workspace), stream, tuning, profiler);
 }
 
 int dsa_indexer_topk(const dsa_indexer_shape* shape, const void* q, const void* k, const float* w,
@@ -251,6 +301,38 @@ int dsa_indexer_scores(const dsa_indexer_shape* shape, const void* q, const void
   return launch_scores(c, stream);
 }
 
+size_t dsa_indexer_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int dsa_indexer_topk_noalloc(const dsa_indexer_shape* shape, const void* q, const void* k,
+                             const float* w, const int32_t* cu_seqlens_q,
+                             const int32_t* cu_seqlens_k, const int32_t* q_pos_offsets,
+                             int32_t topk, int32_t* out_ids, float* out_scores, hipStream_t stream) {
+  int rc = check_inputs(shape, q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets);
+  if (rc) return rc;
+  rc = check_outputs(shape, topk, out_ids, out_scores);
+  if (rc) return rc;
+  if (dsa_indexer_workspace_size(shape) > kScratchBytes) return DSA_ERR_SCRATCH;
+  int dev_id = 0;
+  if (hipGetDevice(&dev_id) != hipSuccess || dev_id < 0 || dev_id >= kMaxDevices) return DSA_ERR_DEVICE;
+  const DeviceInfo* dev = device_info();
+  if (!dev) return DSA_ERR_DEVICE;
+  unsigned char* const ws = scratch_of(dev_id);
+  if (!ws) return DSA_ERR_DEVICE;
+  if (shape->total_q == 0) return DSA_OK;
+  // The counters must be zero at entry: every completed call leaves them so, the first call on
+  // the device clears them (a fill kernel on this stream), and so does the call after a failed
+  // launch.
+  if (!g_scratch_clean[dev_id].load()) {
+    if (dsa::launch_ctrl_init(reinterpret_cast<uint32_t*>(ws), stream) != hipSuccess)
+      return DSA_ERR_LAUNCH;
+    g_scratch_clean[dev_id].store(true);
+  }
+  rc = enqueue_topk(dev, shape, q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets, topk, out_ids,
+                    out_scores, ws, stream, nullptr, nullptr);
+  if (rc == DSA_ERR_LAUNCH) g_scratch_clean[dev_id].store(false);
+  return rc;
+}
+
 const char* dsa_indexer_status_string(int code) {
   switch (code) {
     case DSA_OK: return "ok";
@@ -260,6 +342,9 @@ const char* dsa_indexer_status_string(int code) {
     case DSA_ERR_WORKSPACE: return "workspace too small";
     case DSA_ERR_LAUNCH: return "HIP launch failed (re-initialise the workspace)";
     case DSA_ERR_DEVICE: return "current device is not gfx950";
+    case DSA_ERR_SCRATCH:
+      return "the shape needs more than the fixed scratch of the no-allocation entry point "
+             "(dsa_indexer_noalloc_max_bytes)";
     default: return "unknown status";
   }
 }

@@ -45,6 +45,8 @@ EXPORTED_SYMBOLS = (
     "dsa_indexer_backward_ex",
     "dsa_indexer_sparse_attention",
     "dsa_indexer_sparse_attention_workspace_size",
+    "dsa_indexer_topk_noalloc",
+    "dsa_indexer_noalloc_max_bytes",
 )
 STATUS_BAD_IDS = 0x8
 ATTN_HEADS, ATTN_QK_DIM, ATTN_V_DIM = 128, 576, 512
@@ -117,6 +119,10 @@ def lib():
         L.dsa_indexer_sparse_attention.restype = ctypes.c_int
         L.dsa_indexer_sparse_attention_workspace_size.argtypes = [i32, i32]
         L.dsa_indexer_sparse_attention_workspace_size.restype = sz
+        L.dsa_indexer_topk_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
+        L.dsa_indexer_topk_noalloc.restype = ctypes.c_int
+        L.dsa_indexer_noalloc_max_bytes.argtypes = []
+        L.dsa_indexer_noalloc_max_bytes.restype = sz
         _LIB = L
     return _LIB
 
@@ -265,6 +271,29 @@ def topk(q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets=None, topk: int = 20
                                        None if profiler is None else profiler.handle)
     _check(rc, "dsa_indexer_topk")
     return out_ids, out_scores
+
+
+def topk_noalloc(q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets=None, topk: int = 2048,
+                 max_seqlen_k: int = 0, out_ids: Optional[torch.Tensor] = None,
+                 out_scores: Optional[torch.Tensor] = None):
+    """topk() through the entry point that allocates nothing (the library's fixed per-GPU array)."""
+    dev, T, Tkv, B = _inputs(q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets)
+    if out_ids is None:
+        out_ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    if out_scores is None:
+        out_scores = torch.empty((T, topk), dtype=torch.float32, device=dev)
+    _require(out_ids, "out_ids", torch.int32, (T, topk), dev)
+    _require(out_scores, "out_scores", torch.float32, (T, topk), dev)
+    shape = make_shape(T, Tkv, B, max_seqlen_k)
+    rc = lib().dsa_indexer_topk_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(w), _ptr(cu_seqlens_q),
+                                        _ptr(cu_seqlens_k), _ptr(q_pos_offsets), int(topk), _ptr(out_ids),
+                                        _ptr(out_scores), _stream(dev))
+    _check(rc, "dsa_indexer_topk_noalloc")
+    return out_ids, out_scores
+
+
+def noalloc_max_bytes() -> int:
+    return int(lib().dsa_indexer_noalloc_max_bytes())
 
 
 def scores(q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets=None, max_seqlen_k: int = 0,

@@ -60,6 +60,8 @@ extern "C" {
 #define DSA_ERR_WORKSPACE (-4)  /* workspace_bytes below dsa_indexer_workspace_size()          */
 #define DSA_ERR_LAUNCH (-5)     /* a HIP launch failed; re-run dsa_indexer_workspace_init      */
 #define DSA_ERR_DEVICE (-6)     /* current device is not gfx950 or cannot be queried           */
+#define DSA_ERR_SCRATCH (-7)    /* dsa_indexer_topk_noalloc: the shape needs more than its fixed
+                                   scratch (dsa_indexer_noalloc_max_bytes)                      */
 
 /* Device status bits, left in the workspace control block by the kernels.  They are sticky
    (reporting only; cleared by dsa_indexer_workspace_init): whether a call's segment tables are
@@ -134,6 +136,27 @@ int dsa_indexer_topk(const dsa_indexer_shape* shape, const void* q, const void* 
                      const int32_t* q_pos_offsets, int32_t topk, int32_t* out_ids,
                      float* out_scores, void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
+
+/*
+ * dsa_indexer_topk for callers that cannot allocate device memory or own a workspace: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * results and errors as dsa_indexer_topk, without the workspace: the control block and score
+ * rows live in a fixed device array inside the library, one copy per GPU, held from the first
+ * use of the library on that GPU until the process ends.  Nothing is allocated on any call.
+ *   - A shape whose dsa_indexer_workspace_size exceeds dsa_indexer_noalloc_max_bytes()
+ *     (256 bytes + 64 MiB: e.g. 4096 queries of up to 4096 keys, or 256 of 65536) returns
+ *     DSA_ERR_SCRATCH and enqueues nothing.
+ *   - Every call on a GPU uses that GPU's one array: calls that can overlap on one GPU (other
+ *     streams, other threads) race and must be serialised by the caller.  The first call on a
+ *     GPU, and the call after one that returned DSA_ERR_LAUNCH, also enqueue a small fill kernel
+ *     that zeroes the array's counters; every other call enqueues only the scan's two kernels.
+ */
+int dsa_indexer_topk_noalloc(const dsa_indexer_shape* shape, const void* q, const void* k,
+                             const float* w, const int32_t* cu_seqlens_q,
+                             const int32_t* cu_seqlens_k, const int32_t* q_pos_offsets,
+                             int32_t topk, int32_t* out_ids, float* out_scores, hipStream_t stream);
+/* Bytes of the fixed array dsa_indexer_topk_noalloc works in (the largest workspace size it accepts). */
+size_t dsa_indexer_noalloc_max_bytes(void);
 
 /*
  * Score phase only ("indexer logits"): writes I[t, cu_seqlens_k[b] + j] to

@@ -51,7 +51,7 @@ def test_workspace_size():
 
 def test_status_strings():
     L = ix.lib()
-    for code in range(0, -7, -1):
+    for code in range(0, -8, -1):
         assert L.dsa_indexer_status_string(code)
     assert L.dsa_indexer_status_string(-99) == b"unknown status"
 
