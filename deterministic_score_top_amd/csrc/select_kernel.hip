@@ -64,6 +64,90 @@ __device__ __forceinline__ void wave_prefix3(uint32_t cnt, uint32_t& excl, uint3
 }
 
 
+// Segment tables of batches with at most kSegCache segments, cached in LDS by every block.
+struct SegCache {
+  int32_t cq[kSegCache + 1];
+  int32_t ck[kSegCache + 1];
+  int32_t off[kSegCache];
+};
+
+template <int NT>
+__device__ bool cache_segments(const SelectParams& p, SegCache& sc) {
+  const bool cached = p.B <= kSegCache;
+  if (cached) {
+    for (int i = threadIdx.x; i <= p.B; i += NT) {
+      sc.cq[i] = p.cu_q[i];
+      sc.ck[i] = p.cu_k[i];
+      if (i < p.B) sc.off[i] = p.offs ? p.offs[i] : 0;
+    }
+  }
+  return cached;
+}
+
+// Visible key count n and first key id kb of row t (both wave-uniform); n = 0 when the call's
+// tables are invalid.
+__device__ void row_geometry(const SelectParams& p, const SegCache& sc, bool cached, bool bad, int t,
+                             int& n_out, int& kb_out) {
+  int n = 0, kb = 0;
+  if (!bad) {
+    const int32_t* cq = cached ? sc.cq : p.cu_q;
+    int lo = 0, hi = p.B + 1;  // first segment start beyond t
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (cq[mid] <= t) lo = mid + 1; else hi = mid;
+    }
+    const int b = lo - 1;
+    if (b >= 0 && b < p.B) {
+      const int qb = cq[b];
+      kb = cached ? sc.ck[b] : p.cu_k[b];
+      const int lk = min((cached ? sc.ck[b + 1] : p.cu_k[b + 1]) - kb, p.Lmax);
+      const int off = cached ? sc.off[b] : (p.offs ? p.offs[b] : 0);
+      n = min(max(off + (t - qb) + 1, 0), max(lk, 0));
+    }
+  }
+  n_out = __builtin_amdgcn_readfirstlane(n);  // the same for every lane: keep it scalar
+  kb_out = __builtin_amdgcn_readfirstlane(kb);
+}
+
+// A row with at most topk visible keys: every key is kept, the rest of the row is padding.  A
+// thread's row loads are issued four at a time before their stores.
+template <int NT>
+__device__ void copy_row(const uint32_t* row, int n, int kb, int topk, int32_t* oid, float* osc) {
+  const int tid = threadIdx.x;
+  constexpr int kCopyPer = (kMaxTopk + NT - 1) / NT;
+  constexpr int kBatch = kCopyPer < 4 ? kCopyPer : 4;
+#pragma unroll
+  for (int i0 = 0; i0 < kCopyPer; i0 += kBatch) {
+    uint32_t kv[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int j = tid + (i0 + i) * NT;
+      kv[i] = j < n ? row[j] : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int j = tid + (i0 + i) * NT;
+      if (j < n) {
+        oid[j] = kb + j;
+        osc[j] = key_value(kv[i]);
+      } else if (j < topk) {
+        oid[j] = -1;
+        osc[j] = -__builtin_inff();
+      }
+    }
+  }
+}
+
+// Block 0: the score kernel drew units + grid tickets; anything else means the counter was not
+// zero when it started.  Reset for the next call (this kernel runs after the score kernel).
+__device__ void check_reset_counter(const SelectParams& p) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (p.ctrl[kCtrlTicket] != p.ctrl[kCtrlExpected]) atomicOr(p.ctrl + kCtrlStatus, kStatusCorruptCounter);
+    p.ctrl[kCtrlTicket] = 0u;
+    p.ctrl[kCtrlDone] = 0u;
+  }
+}
+
 template <int NT>
 struct alignas(16) Smem {
   static constexpr int NW = NT / 64;
@@ -76,16 +160,14 @@ struct alignas(16) Smem {
   // [4..6] sample statistics, [7..8] compaction count and row maximum
   uint32_t wred[NW][12];
   uint32_t bcast[8];
-  int32_t cq[kSegCache + 1];
-  int32_t ck[kSegCache + 1];
-  int32_t off[kSegCache];
+  SegCache seg;
 };
 
 // Locate the bin holding rank krem (1-based, from the top) in hist[0..nb): returns
 // (bin, count above it, count in it) through bcast.  Thread tid owns bins
 // [nb - (tid+1)*per, nb - tid*per).
-template <int NT>
-__device__ void find_bin(Smem<NT>& sm, int nb, uint32_t krem) {
+template <int NT, class SM>
+__device__ void find_bin(SM& sm, int nb, uint32_t krem) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int per = nb >= NT ? nb / NT : 1;
   const int lo = nb - (tid + 1) * per;
@@ -105,7 +187,7 @@ __device__ void find_bin(Smem<NT>& sm, int nb, uint32_t krem) {
   __syncthreads();
   uint32_t above = incl - local;
 #pragma unroll
-  for (int i = 0; i < Smem<NT>::NW; ++i) above += i < wv ? sm.wred[i][0] : 0u;
+  for (int i = 0; i < NT / 64; ++i) above += i < wv ? sm.wred[i][0] : 0u;
   if (lo >= 0 && above < krem && krem <= above + local) {
     for (int d = lo + per - 1; d >= lo; --d) {
       const uint32_t h = sm.hist[d];
@@ -231,13 +313,13 @@ __device__ void resolve_all(Smem<NT>& sm, const KS& ks, int topk, uint32_t& T, u
 }
 
 // Output offsets of this wave: selected keys of waves before it, and equal keys before it.
-template <int NT>
-__device__ void wave_bases(Smem<NT>& sm, uint32_t eq_skip, uint32_t& sel_base, uint32_t& eq_base) {
+template <int NT, class SM>
+__device__ void wave_bases(SM& sm, uint32_t eq_skip, uint32_t& sel_base, uint32_t& eq_base) {
   const int wv = threadIdx.x >> 6;
   sel_base = 0;
   eq_base = 0;
 #pragma unroll
-  for (int i = 0; i < Smem<NT>::NW; ++i) {
+  for (int i = 0; i < NT / 64; ++i) {
     if (i < wv) {
       const uint32_t g_i = sm.wred[i][2], e_i = sm.wred[i][3];
       const uint32_t take = (eq_base + e_i > eq_skip) ? min(e_i, eq_base + e_i - eq_skip) : 0u;
@@ -255,73 +337,18 @@ __global__ __launch_bounds__(NT, NT == 256 ? 6 : 1) void select_kernel(SelectPar
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int topk = p.topk;
   const bool bad = p.ctrl[kCtrlCallBad] != 0u;  // this call's tables are invalid: all rows padding
-  if (blockIdx.x == 0 && tid == 0) {
-    // the score kernel drew units + grid tickets; anything else means the counter was not zero
-    // when it started.  Reset for the next call (this kernel runs after the score kernel).
-    if (p.ctrl[kCtrlTicket] != p.ctrl[kCtrlExpected]) atomicOr(p.ctrl + kCtrlStatus, kStatusCorruptCounter);
-    p.ctrl[kCtrlTicket] = 0u;
-    p.ctrl[kCtrlDone] = 0u;
-  }
-  const bool cached = p.B <= kSegCache;
-  if (cached) {
-    for (int i = tid; i <= p.B; i += NT) {
-      sm.cq[i] = p.cu_q[i];
-      sm.ck[i] = p.cu_k[i];
-      if (i < p.B) sm.off[i] = p.offs ? p.offs[i] : 0;
-    }
-  }
+  check_reset_counter(p);
+  const bool cached = cache_segments<NT>(p, sm.seg);
   __syncthreads();
 
   for (int t = blockIdx.x; t < p.T; t += gridDim.x) {
-    // ---- row geometry ----------------------------------------------------------------------
-    int n = 0, kb = 0;
-    if (!bad) {
-      const int32_t* cq = cached ? sm.cq : p.cu_q;
-      int lo = 0, hi = p.B + 1;  // first segment start beyond t
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (cq[mid] <= t) lo = mid + 1; else hi = mid;
-      }
-      const int b = lo - 1;
-      if (b >= 0 && b < p.B) {
-        const int qb = cq[b];
-        kb = cached ? sm.ck[b] : p.cu_k[b];
-        const int lk = min((cached ? sm.ck[b + 1] : p.cu_k[b + 1]) - kb, p.Lmax);
-        const int off = cached ? sm.off[b] : (p.offs ? p.offs[b] : 0);
-        n = min(max(off + (t - qb) + 1, 0), max(lk, 0));
-      }
-    }
-    n = __builtin_amdgcn_readfirstlane(n);  // the same for every lane: keep it scalar
-    kb = __builtin_amdgcn_readfirstlane(kb);
+    int n, kb;
+    row_geometry(p, sm.seg, cached, bad, t, n, kb);
     const uint32_t* const row = p.keys + (int64_t)t * p.ld;
     int32_t* const oid = p.out_ids + (int64_t)t * topk;
     float* const osc = p.out_scores + (int64_t)t * topk;
     if (n <= topk) {  // every visible key is kept; pad the rest
-      // a thread's row loads are issued four at a time before their stores (two memory round
-      // trips instead of eight; four keeps the kernel within the registers of six row blocks
-      // per CU)
-      constexpr int kCopyPer = (kMaxTopk + NT - 1) / NT;
-      constexpr int kBatch = kCopyPer < 4 ? kCopyPer : 4;
-#pragma unroll
-      for (int i0 = 0; i0 < kCopyPer; i0 += kBatch) {
-        uint32_t kv[kBatch];
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-          const int j = tid + (i0 + i) * NT;
-          kv[i] = j < n ? row[j] : 0u;
-        }
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-          const int j = tid + (i0 + i) * NT;
-          if (j < n) {
-            oid[j] = kb + j;
-            osc[j] = key_value(kv[i]);
-          } else if (j < topk) {
-            oid[j] = -1;
-            osc[j] = -__builtin_inff();
-          }
-        }
-      }
+      copy_row<NT>(row, n, kb, topk, oid, osc);
       continue;
     }
 
@@ -617,9 +644,9 @@ hipError_t select_occupancy(SelectOccupancy* occ) {
 
 hipError_t launch_select(const SelectParams& p, int cus, const SelectOccupancy& occ, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
-  // Few rows (a split tail, a handful of decode queries) leave most CUs idle: give each row
-  // 16 waves instead of 4, so its passes over the keys take a quarter of the steps.
   if (4 * p.T <= cus) {
+    // Few rows (a split tail, a handful of decode queries) leave most CUs idle: give each row
+    // 16 waves instead of 4, so its passes over the keys take a quarter of the steps.
     hipLaunchKernelGGL((select_kernel<1024>), dim3(min(p.T, cus * occ.wide * 4)), dim3(1024), 0, s, p);
   } else {
     hipLaunchKernelGGL((select_kernel<256>), dim3(min(p.T, cus * occ.narrow * 4)), dim3(256), 0, s, p);

@@ -99,6 +99,17 @@ def test_select_long_rows_exact(distinct, nk, topk):
     _check_all(wl, exact=True)
 
 
+@pytest.mark.parametrize("distinct", [None, 16, 2, 1])
+@pytest.mark.parametrize("nk", [3000, 6000, 12000])
+def test_select_many_long_rows_exact(distinct, nk):
+    # 80 rows (more than a quarter of the CUs: the 256-thread select blocks) of 3000 to 12000
+    # keys on exact scores; few distinct key vectors give long runs of equal scores across the
+    # k-th key (the larger-id rule decides) and push the sampled threshold into its fallback
+    wl = W.integer_valued([50, 30], [nk, nk // 2], [nk - 50, nk // 2 - 40], topk=2048 if nk > 3000 else 700,
+                          seed=nk + (distinct or 0), distinct_keys=distinct)
+    _check_all(wl, exact=True)
+
+
 def test_scores_export():
     wl = W.random_segments([21, 11], [90, 140], [40, 0], topk=8, seed=5)
     q, k, w, cq, ck, offs = _dev(wl)
