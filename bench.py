@@ -407,6 +407,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warmup-s", type=float, default=2.0,
                     help="after the --warmup calls, keep warming up until this many seconds have passed")
+    ap.add_argument("--call", choices=("eager", "prepared"), default="eager",
+                    help="eager: dsa_indexer_topk per call; prepared: one dsa_indexer_prepare, then dsa_indexer_run")
     ap.add_argument("--no-gate", action="store_true",
                     help="skip the N=16384 score-kernel measurement that the headline run adds")
     ap.add_argument("--hold-cus", type=int, default=0,
@@ -454,13 +456,39 @@ def main():
     q, k, w = wl.q.to(dev), wl.k.to(dev), wl.w.to(dev)
     cq, ck = wl.cu_seqlens_q.to(dev), wl.cu_seqlens_k.to(dev)
     offs = None if wl.q_pos_offsets is None else wl.q_pos_offsets.to(dev)
-    ws = ix.alloc_workspace(wl.T, wl.Tkv, wl.B, wl.max_seqlen_k, dev)
     out_ids = torch.empty((wl.T, wl.topk), dtype=torch.int32, device=dev)
     out_sc = torch.empty((wl.T, wl.topk), dtype=torch.float32, device=dev)
-    call = dict(topk=wl.topk, workspace=ws, max_seqlen_k=wl.max_seqlen_k, out_ids=out_ids, out_scores=out_sc)
+    if args.call == "prepared":
+        # the prepared runner: arguments bound and the plan stored once; each call only launches
+        runner = ix.prepare(q, k, w, cq, ck, offs, topk=wl.topk, max_seqlen_k=wl.max_seqlen_k,
+                            out_ids=out_ids, out_scores=out_sc)
+        ws = runner.workspace
+
+        def topk_call(profiler=None):
+            runner.run(profiler)
+    else:
+        ws = ix.alloc_workspace(wl.T, wl.Tkv, wl.B, wl.max_seqlen_k, dev)
+        call = dict(topk=wl.topk, workspace=ws, max_seqlen_k=wl.max_seqlen_k, out_ids=out_ids, out_scores=out_sc)
+
+        def topk_call(profiler=None):
+            ix.topk(q, k, w, cq, ck, offs, profiler=profiler, **call)
 
     flush = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev) if args.cold else None
-    warm_calls, warm_s = warm_up(lambda: ix.topk(q, k, w, cq, ck, offs, **call), args.warmup, args.warmup_s)
+    warm_calls, warm_s = warm_up(topk_call, args.warmup, args.warmup_s)
+    # host path per call: enqueue cost of back-to-back calls (no synchronisation in between), and
+    # the wall time of one synchronised call (host path + GPU + completion), median of 100
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(100):
+        topk_call()
+    host_us = (time.perf_counter() - t0) * 1e4
+    torch.cuda.synchronize()
+    sync_wall = []
+    for _ in range(100):
+        t0 = time.perf_counter()
+        topk_call()
+        torch.cuda.synchronize()
+        sync_wall.append((time.perf_counter() - t0) * 1e3)
     hold = None
     if args.hold_cus > 0:
         import ctypes
@@ -469,7 +497,7 @@ def main():
         hold.spinner_wait_resident.argtypes = [ctypes.c_double]
         wprof = ix.Profiler(20)
         for _ in range(20):
-            ix.topk(q, k, w, cq, ck, offs, profiler=wprof, **call)
+            topk_call(wprof)
         a, b = wprof.read_calls()
         wprof.close()
         hold_us = args.hold_frac * 1000.0 * sorted(x + y for x, y in zip(a, b))[len(a) // 2]
@@ -484,7 +512,7 @@ def main():
             torch.cuda.synchronize()
             if hold.spinner_start(args.hold_cus, hold_us) != 0 or hold.spinner_wait_resident(1000.0) != 0:
                 raise SystemExit("bench: could not start the CU holder")
-        ix.topk(q, k, w, cq, ck, offs, profiler=prof, **call)
+        topk_call(prof)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     per_score, per_select = prof.read_calls()
@@ -528,6 +556,9 @@ def main():
         "frac_bf16_peak_call": eff_call / PEAK_BF16_TFLOPS,
         "score_kernel_ms": score_avg_ms,
         "select_kernel_ms": select_avg_ms,
+        "call": args.call,
+        "host_enqueue_us_per_call": host_us,
+        "sync_call_wall_ms_p50": _pct(sync_wall, 0.5),
         "warmup_calls_run": warm_calls,
         "warmup_s_run": warm_s,
         "score_kernel_ms_per_call": {"first5": per_score[:5], "last5": per_score[-5:],

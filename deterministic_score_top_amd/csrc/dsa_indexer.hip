@@ -154,6 +154,7 @@ int launch_scores(const Call& c, hipStream_t stream) {
   p.chunk_tiles = chunk;
   p.max_tiles = max_tiles;
   p.store_keys = c.store_keys;
+  p.plan = nullptr;
   if (dsa::launch_score(p, grid, smem, stream) != hipSuccess) return DSA_ERR_LAUNCH;
   return DSA_OK;
 }
@@ -194,6 +195,17 @@ struct dsa_indexer_profiler {
   int capacity = 0;
   int used = 0;
   std::vector<hipEvent_t> ev;  // 3 per slot: before score, between, after select
+};
+
+// A prepared runner: both kernels' arguments built once, the plan stored in the workspace.
+struct dsa_indexer_runner {
+  dsa::ScoreParams score;
+  dsa::SelectParams select;
+  int grid = 0;
+  size_t smem = 0;
+  int cus = 0;
+  dsa::SelectOccupancy occ;
+  int total_q = 0;
 };
 
 namespace {
@@ -299,6 +311,105 @@ int dsa_indexer_scores(const dsa_indexer_shape* shape, const void* q, const void
   Call c{shape, q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets, out_scores, ld_out,
          static_cast<uint32_t*>(workspace), nullptr, 0};
   return launch_scores(c, stream);
+}
+
+size_t dsa_indexer_prepared_workspace_size(const dsa_indexer_shape* shape) {
+  const size_t base = dsa_indexer_workspace_size(shape);
+  if (base == 0) return 0;
+  return base + dsa::plan_bytes(shape->num_segments, max_tiles_of(shape));
+}
+
+int dsa_indexer_prepare(const dsa_indexer_shape* shape, const void* q, const void* k, const float* w,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        const int32_t* q_pos_offsets, int32_t topk, int32_t* out_ids,
+                        float* out_scores, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream, dsa_indexer_runner** runner) {
+  if (!runner) return DSA_ERR_NULL;
+  *runner = nullptr;
+  int rc = check_common(shape, q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets, workspace);
+  if (rc) return rc;
+  rc = check_outputs(shape, topk, out_ids, out_scores);
+  if (rc) return rc;
+  if (workspace_bytes < dsa_indexer_prepared_workspace_size(shape)) return DSA_ERR_WORKSPACE;
+  const DeviceInfo* dev = device_info();
+  if (!dev) return DSA_ERR_DEVICE;
+  const int max_tiles = max_tiles_of(shape);
+  const size_t smem = dsa::score_smem_bytes(shape->num_segments, max_tiles);
+  if (smem > dsa::score_smem_limit()) return DSA_ERR_SHAPE;
+
+  unsigned char* const ws = static_cast<unsigned char*>(workspace);
+  const int64_t ld = row_stride(shape);
+  uint32_t* const plan = reinterpret_cast<uint32_t*>(ws + dsa_indexer_workspace_size(shape));
+  dsa_indexer_runner* r = new dsa_indexer_runner();
+  r->grid = dev->cus * dev->score_blocks_per_cu;
+  r->smem = smem;
+  r->cus = dev->cus;
+  r->occ = dev->select;
+  r->total_q = shape->total_q;
+  dsa::ScoreParams& p = r->score;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.w = w;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.offs = q_pos_offsets;
+  p.out = reinterpret_cast<float*>(ws + dsa::kCtrlBytes);
+  p.ld = ld;
+  p.ctrl = reinterpret_cast<uint32_t*>(ws);
+  p.B = shape->num_segments;
+  p.T = shape->total_q;
+  p.Tkv = shape->total_k;
+  p.Lmax = (int32_t)lmax_of(shape);
+  p.chunk_tiles = 0;
+  p.max_tiles = max_tiles;
+  p.store_keys = 1;
+  p.plan = plan;
+  dsa::SelectParams& sp = r->select;
+  sp.keys = reinterpret_cast<const uint32_t*>(p.out);
+  sp.ld = ld;
+  sp.cu_q = cu_seqlens_q;
+  sp.cu_k = cu_seqlens_k;
+  sp.offs = q_pos_offsets;
+  sp.out_ids = out_ids;
+  sp.out_scores = out_scores;
+  sp.ctrl = p.ctrl;
+  sp.B = shape->num_segments;
+  sp.T = shape->total_q;
+  sp.Tkv = shape->total_k;
+  sp.Lmax = p.Lmax;
+  sp.topk = topk;
+  if (dsa::launch_plan(p, r->grid, plan, stream) != hipSuccess) {
+    delete r;
+    return DSA_ERR_LAUNCH;
+  }
+  *runner = r;
+  return DSA_OK;
+}
+
+int dsa_indexer_run_ex(dsa_indexer_runner* runner, hipStream_t stream, dsa_indexer_profiler* profiler) {
+  if (!runner) return DSA_ERR_NULL;
+  if (profiler && profiler->used >= profiler->capacity) return DSA_ERR_SHAPE;
+  if (runner->total_q == 0) return DSA_OK;
+  hipEvent_t* ev = profiler ? &profiler->ev[3 * profiler->used] : nullptr;
+  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return DSA_ERR_LAUNCH;
+  if (dsa::launch_score(runner->score, runner->grid, runner->smem, stream) != hipSuccess) return DSA_ERR_LAUNCH;
+  if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return DSA_ERR_LAUNCH;
+  if (dsa::launch_select(runner->select, runner->cus, runner->occ, stream) != hipSuccess) return DSA_ERR_LAUNCH;
+  if (ev) {
+    if (hipEventRecord(ev[2], stream) != hipSuccess) return DSA_ERR_LAUNCH;
+    profiler->used++;
+  }
+  return DSA_OK;
+}
+
+int dsa_indexer_run(dsa_indexer_runner* runner, hipStream_t stream) {
+  return dsa_indexer_run_ex(runner, stream, nullptr);
+}
+
+int dsa_indexer_runner_destroy(dsa_indexer_runner* runner) {
+  if (!runner) return DSA_ERR_NULL;
+  delete runner;
+  return DSA_OK;
 }
 
 size_t dsa_indexer_noalloc_max_bytes(void) { return kScratchBytes; }

@@ -51,6 +51,7 @@ struct ScoreParams {
   int32_t chunk_tiles;  // keys per unit = chunk_tiles * kTileKeys; 0 = chosen by the kernel
   int32_t max_tiles;    // capacity of the LDS tile table
   int32_t store_keys;   // 1: store order-preserving 32-bit keys instead of FP32 scores
+  const uint32_t* plan; // prepared plan (from launch_plan for this grid), or null: derive it
 };
 
 struct SelectParams {
@@ -140,6 +141,11 @@ size_t score_smem_limit();
 hipError_t score_prepare(size_t max_smem);
 hipError_t score_occupancy(int* blocks_per_cu, size_t smem);
 hipError_t launch_score(const ScoreParams& p, int grid, size_t smem, hipStream_t s);
+// Bytes of a prepared plan for B segments and a tile table of max_tiles entries (a multiple of 256).
+size_t plan_bytes(int B, int max_tiles);
+// One block: derives the plan of `p` for a score launch of `grid` blocks into `out` and zeroes
+// p.ctrl.
+hipError_t launch_plan(const ScoreParams& p, int grid, uint32_t* out, hipStream_t s);
 
 // Resident blocks per CU of the select kernel variants (queried once per device).
 struct SelectOccupancy {

@@ -132,30 +132,25 @@ __device__ void block_scan_excl(uint32_t* arr, int n, uint32_t* part) {
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* const kbuf0 = smem;
-  unsigned char* const kbuf1 = smem + kKBufBytes;
-  unsigned char* const kbuf2 = smem + 2 * kKBufBytes;
-  int* const slot = reinterpret_cast<int*>(smem + kKBufs * kKBufBytes);
-  uint32_t* const part = reinterpret_cast<uint32_t*>(slot + kSlotInts);
-  uint32_t* const seg_tp = part + kPartEntries;                   // B + 1 entries
-  uint32_t* const seg_ord = seg_tp + ((p.B + 1 + 3) & ~3);        // B entries
-  uint32_t* const unit_pf = seg_ord + ((p.B + 3) & ~3);           // max_tiles + 1 entries
+// The work decomposition of a batch (every block of a launch derives the same one from the
+// segment tables; the plan kernel derives it once for a prepared runner): validates the tables,
+// orders segments longest tile first, counts each query tile's key tiles, picks the key chunk
+// for a persistent grid of `grid` blocks and builds the unit prefix.  Leaves seg_tp (tile prefix
+// per segment in that order), seg_ord and unit_pf (unit prefix per tile) in LDS.
+struct PlanInfo {
+  uint32_t units;
+  int ntiles;
+  int chunk_tiles;
+  bool whole_tiles;  // every tile is exactly one unit
+  int flags;         // bit 0: invalid tables, bit 1: a segment longer than Lmax
+};
 
+__device__ PlanInfo compute_plan(const ScoreParams& p, uint32_t grid, int* slot, uint32_t* part, uint32_t* seg_tp,
+                                 uint32_t* seg_ord, uint32_t* unit_pf) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  // wave index, explicitly wave-uniform so per-wave values (query row, buffer resources) live
-  // in scalar registers
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int B = p.B;
-
-  // ---- per-block plan: validate segments, tiles per segment, units per tile -------------
-  // (the block's first ticket is drawn now; its latency overlaps the plan)
-  if (tid == 0) {
-    slot[2] = 0;
-    slot[0] = (int)atomicAdd(p.ctrl + kCtrlTicket, 1u);
-  }
+  if (tid == 0) slot[2] = 0;
   __syncthreads();
   {
     int flags = 0;
@@ -260,10 +255,10 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
     int chunk_tiles = p.chunk_tiles;
     if (chunk_tiles <= 0) {
       const uint32_t total = (uint32_t)slot[3], longest = max((uint32_t)slot[6], 1u);
-      const uint32_t share = total / gridDim.x;
+      const uint32_t share = total / grid;
       chunk_tiles = (int)longest;
-      if (ntiles <= (int)gridDim.x) {
-        uint32_t c = max((total + gridDim.x - 1) / gridDim.x, 1u);
+      if (ntiles <= (int)grid) {
+        uint32_t c = max((total + grid - 1) / grid, 1u);
         for (int it = 0; it < kMaxChunkSearch && c < longest; ++it, ++c) {
           uint32_t n_units = 0;
           for (int g = tid; g < ntiles; g += kScoreThreads) n_units += (unit_pf[g] + c - 1) / c;
@@ -273,7 +268,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
           __syncthreads();
           if (lane == 0) atomicAdd(reinterpret_cast<uint32_t*>(&slot[7]), n_units);
           __syncthreads();
-          if ((uint32_t)slot[7] <= gridDim.x) break;
+          if ((uint32_t)slot[7] <= grid) break;
         }
         chunk_tiles = (int)min(c, longest);
       } else if (5 * longest > 3 * share) {
@@ -297,6 +292,86 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
     block_scan_excl(unit_pf, ntiles, part);
     units = unit_pf[ntiles];
   }
+  PlanInfo info;
+  info.units = units;
+  info.ntiles = ntiles;
+  info.chunk_tiles = chunk_keys / kTileKeys;
+  info.whole_tiles = whole_tiles;
+  info.flags = plan_flags;
+  return info;
+}
+
+// Header of a prepared plan (u32 words at the plan's start), followed by copies of the segment
+// tables the plan was derived from (cu_q[B+1], cu_k[B+1], offsets[B]) and then seg_tp[B+1],
+// seg_ord[B], unit_pf[ntiles+1].
+constexpr int kPlanUnits = 0, kPlanTiles = 1, kPlanChunk = 2, kPlanWhole = 3, kPlanFlags = 4, kPlanGrid = 5,
+              kPlanB = 6, kPlanHeader = 16;
+
+__device__ __forceinline__ int plan_tables_at(int B) { return kPlanHeader; }
+__device__ __forceinline__ int plan_arrays_at(int B) { return kPlanHeader + 3 * B + 2; }
+
+// Prepared path: the plan the prepare step stored, if the tables it was derived from still hold
+// the live values and it was made for this grid (else returns false and nothing is loaded).
+__device__ bool load_plan(const ScoreParams& p, int* slot, uint32_t* seg_tp, uint32_t* seg_ord, uint32_t* unit_pf,
+                          PlanInfo& info) {
+  const int tid = threadIdx.x;
+  const int B = p.B;
+  const uint32_t* const hdr = p.plan;
+  const uint32_t* const tab = p.plan + plan_tables_at(B);
+  if (tid == 0) slot[9] = (hdr[kPlanGrid] != gridDim.x || hdr[kPlanB] != (uint32_t)B) ? 1 : 0;
+  __syncthreads();
+  int diff = 0;
+  for (int i = tid; i <= B; i += kScoreThreads) {
+    diff |= (uint32_t)p.cu_q[i] != tab[i];
+    diff |= (uint32_t)p.cu_k[i] != tab[B + 1 + i];
+    if (i < B) diff |= (uint32_t)(p.offs ? p.offs[i] : 0) != tab[2 * B + 2 + i];
+  }
+  if (diff) atomicOr(&slot[9], 1);
+  __syncthreads();
+  if (slot[9]) return false;
+  info.units = hdr[kPlanUnits];
+  info.ntiles = (int)hdr[kPlanTiles];
+  info.chunk_tiles = (int)hdr[kPlanChunk];
+  info.whole_tiles = hdr[kPlanWhole] != 0;
+  info.flags = (int)hdr[kPlanFlags];
+  const uint32_t* const arr = p.plan + plan_arrays_at(B);
+  const int nseg = B + 1, nord = B, nunit = (info.flags & 1) ? 0 : info.ntiles + 1;
+  for (int i = tid; i < nseg; i += kScoreThreads) seg_tp[i] = arr[i];
+  for (int i = tid; i < nord; i += kScoreThreads) seg_ord[i] = arr[nseg + i];
+  for (int i = tid; i < nunit; i += kScoreThreads) unit_pf[i] = arr[nseg + nord + i];
+  __syncthreads();
+  return true;
+}
+
+__global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* const kbuf0 = smem;
+  unsigned char* const kbuf1 = smem + kKBufBytes;
+  unsigned char* const kbuf2 = smem + 2 * kKBufBytes;
+  int* const slot = reinterpret_cast<int*>(smem + kKBufs * kKBufBytes);
+  uint32_t* const part = reinterpret_cast<uint32_t*>(slot + kSlotInts);
+  uint32_t* const seg_tp = part + kPartEntries;                   // B + 1 entries
+  uint32_t* const seg_ord = seg_tp + ((p.B + 1 + 3) & ~3);        // B entries
+  uint32_t* const unit_pf = seg_ord + ((p.B + 3) & ~3);           // max_tiles + 1 entries
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // wave index, explicitly wave-uniform so per-wave values (query row, buffer resources) live
+  // in scalar registers
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int B = p.B;
+
+  // ---- per-block plan (the block's first ticket is drawn now; its latency overlaps the plan):
+  // the prepared one when it still applies, else derived from the tables here
+  if (tid == 0) slot[0] = (int)atomicAdd(p.ctrl + kCtrlTicket, 1u);
+  PlanInfo info;
+  if (!(p.plan && load_plan(p, slot, seg_tp, seg_ord, unit_pf, info)))
+    info = compute_plan(p, gridDim.x, slot, part, seg_tp, seg_ord, unit_pf);
+  const int plan_flags = info.flags;
+  const uint32_t units = info.units;
+  const int ntiles = info.ntiles;
+  const int chunk_keys = info.chunk_tiles * kTileKeys;
+  const bool whole_tiles = info.whole_tiles;
   // this call's verdict on its tables, for the select kernel (always overwritten, so a bad call
   // does not affect later calls on the same workspace)
   if (blockIdx.x == 0 && tid == 0) p.ctrl[kCtrlCallBad] = (plan_flags & 1) ? 1u : 0u;
@@ -544,6 +619,42 @@ __global__ void ctrl_init_kernel(uint32_t* ctrl) {
   if (threadIdx.x < kCtrlBytes / 4) ctrl[threadIdx.x] = 0u;
 }
 
+// Prepare step of a runner: one block derives the plan for a launch of `grid` blocks, stores it
+// with the tables it came from at `out`, and zeroes the control block (the ticket word is zeroed
+// once here; every run leaves it at zero again).
+__global__ __launch_bounds__(kScoreThreads) void plan_kernel(ScoreParams p, uint32_t grid, uint32_t* out) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int* const slot = reinterpret_cast<int*>(smem);
+  uint32_t* const part = reinterpret_cast<uint32_t*>(slot + kSlotInts);
+  uint32_t* const seg_tp = part + kPartEntries;
+  uint32_t* const seg_ord = seg_tp + ((p.B + 1 + 3) & ~3);
+  uint32_t* const unit_pf = seg_ord + ((p.B + 3) & ~3);
+  const int tid = threadIdx.x;
+  const int B = p.B;
+  if (tid < kCtrlBytes / 4) p.ctrl[tid] = 0u;
+  const PlanInfo info = compute_plan(p, grid, slot, part, seg_tp, seg_ord, unit_pf);
+  if (tid == 0) {
+    out[kPlanUnits] = info.units;
+    out[kPlanTiles] = (uint32_t)info.ntiles;
+    out[kPlanChunk] = (uint32_t)info.chunk_tiles;
+    out[kPlanWhole] = info.whole_tiles ? 1u : 0u;
+    out[kPlanFlags] = (uint32_t)info.flags;
+    out[kPlanGrid] = grid;
+    out[kPlanB] = (uint32_t)B;
+  }
+  uint32_t* const tab = out + plan_tables_at(B);
+  for (int i = tid; i <= B; i += kScoreThreads) {
+    tab[i] = (uint32_t)p.cu_q[i];
+    tab[B + 1 + i] = (uint32_t)p.cu_k[i];
+    if (i < B) tab[2 * B + 2 + i] = (uint32_t)(p.offs ? p.offs[i] : 0);
+  }
+  uint32_t* const arr = out + plan_arrays_at(B);
+  const int nseg = B + 1, nord = B, nunit = (info.flags & 1) ? 0 : info.ntiles + 1;
+  for (int i = tid; i < nseg; i += kScoreThreads) arr[i] = seg_tp[i];
+  for (int i = tid; i < nord; i += kScoreThreads) arr[nseg + i] = seg_ord[i];
+  for (int i = tid; i < nunit; i += kScoreThreads) arr[nseg + nord + i] = unit_pf[i];
+}
+
 }  // namespace
 
 size_t score_smem_bytes(int B, int max_tiles) {
@@ -553,8 +664,22 @@ size_t score_smem_bytes(int B, int max_tiles) {
 
 size_t score_smem_limit() { return 144 * 1024; }
 
+size_t plan_bytes(int B, int max_tiles) {
+  const size_t words = (size_t)kPlanHeader + 3 * (size_t)B + 2 + (size_t)(B + 1) + (size_t)B + (size_t)max_tiles + 1;
+  return (words * 4 + 255) / 256 * 256;
+}
+
+hipError_t launch_plan(const ScoreParams& p, int grid, uint32_t* out, hipStream_t s) {
+  const size_t smem = score_smem_bytes(p.B, p.max_tiles) - (size_t)kKBufs * kKBufBytes;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kScoreThreads), smem, s, p, (uint32_t)grid, out);
+  return hipGetLastError();
+}
+
 hipError_t score_prepare(size_t max_smem) {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_smem);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&plan_kernel),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_smem);
 }
 

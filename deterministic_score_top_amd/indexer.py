@@ -47,6 +47,11 @@ EXPORTED_SYMBOLS = (
     "dsa_indexer_sparse_attention_workspace_size",
     "dsa_indexer_topk_noalloc",
     "dsa_indexer_noalloc_max_bytes",
+    "dsa_indexer_prepared_workspace_size",
+    "dsa_indexer_prepare",
+    "dsa_indexer_run",
+    "dsa_indexer_run_ex",
+    "dsa_indexer_runner_destroy",
 )
 STATUS_BAD_IDS = 0x8
 ATTN_HEADS, ATTN_QK_DIM, ATTN_V_DIM = 128, 576, 512
@@ -123,6 +128,16 @@ def lib():
         L.dsa_indexer_topk_noalloc.restype = ctypes.c_int
         L.dsa_indexer_noalloc_max_bytes.argtypes = []
         L.dsa_indexer_noalloc_max_bytes.restype = sz
+        L.dsa_indexer_prepared_workspace_size.argtypes = [sp]
+        L.dsa_indexer_prepared_workspace_size.restype = sz
+        L.dsa_indexer_prepare.argtypes = [sp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp, ctypes.POINTER(vp)]
+        L.dsa_indexer_prepare.restype = ctypes.c_int
+        L.dsa_indexer_run.argtypes = [vp, vp]
+        L.dsa_indexer_run.restype = ctypes.c_int
+        L.dsa_indexer_run_ex.argtypes = [vp, vp, vp]
+        L.dsa_indexer_run_ex.restype = ctypes.c_int
+        L.dsa_indexer_runner_destroy.argtypes = [vp]
+        L.dsa_indexer_runner_destroy.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -271,6 +286,72 @@ def topk(q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets=None, topk: int = 20
                                        None if profiler is None else profiler.handle)
     _check(rc, "dsa_indexer_topk")
     return out_ids, out_scores
+
+
+def prepared_workspace_size(T: int, Tkv: int, B: int, max_seqlen_k: int = 0) -> int:
+    s = make_shape(T, Tkv, B, max_seqlen_k)
+    n = lib().dsa_indexer_prepared_workspace_size(ctypes.byref(s))
+    if n == 0:
+        raise DsaError(-3, "prepared_workspace_size")
+    return int(n)
+
+
+class Runner:
+    """A prepared top-k call (dsa_indexer_prepare): bound tensors, plan stored in the workspace.
+
+    run() enqueues the scan's two kernels on the current stream and returns (out_ids, out_scores).
+    The tensors stay referenced by the runner; their values may change between runs.
+    """
+
+    def __init__(self, q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets=None, topk: int = 2048,
+                 max_seqlen_k: int = 0, out_ids: Optional[torch.Tensor] = None,
+                 out_scores: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+        dev, T, Tkv, B = _inputs(q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets)
+        if out_ids is None:
+            out_ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
+        if out_scores is None:
+            out_scores = torch.empty((T, topk), dtype=torch.float32, device=dev)
+        _require(out_ids, "out_ids", torch.int32, (T, topk), dev)
+        _require(out_scores, "out_scores", torch.float32, (T, topk), dev)
+        if workspace is None:
+            workspace = torch.empty(prepared_workspace_size(T, Tkv, B, max_seqlen_k), dtype=torch.uint8, device=dev)
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+        self.handle = None
+        self.device = dev
+        self.tensors = (q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets, out_ids, out_scores, workspace)
+        self.out_ids, self.out_scores, self.workspace = out_ids, out_scores, workspace
+        shape = make_shape(T, Tkv, B, max_seqlen_k)
+        h = ctypes.c_void_p()
+        _check(lib().dsa_indexer_prepare(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(w), _ptr(cu_seqlens_q),
+                                         _ptr(cu_seqlens_k), _ptr(q_pos_offsets), int(topk), _ptr(out_ids),
+                                         _ptr(out_scores), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(dev),
+                                         ctypes.byref(h)), "dsa_indexer_prepare")
+        self.handle = h
+
+    def run(self, profiler: Optional["Profiler"] = None):
+        if profiler is None:
+            rc = lib().dsa_indexer_run(self.handle, _stream(self.device))
+        else:
+            rc = lib().dsa_indexer_run_ex(self.handle, _stream(self.device), profiler.handle)
+        _check(rc, "dsa_indexer_run")
+        return self.out_ids, self.out_scores
+
+    def close(self):
+        if self.handle:
+            lib().dsa_indexer_runner_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def prepare(q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets=None, topk: int = 2048, **kw) -> Runner:
+    return Runner(q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets, topk, **kw)
 
 
 def topk_noalloc(q, k, w, cu_seqlens_q, cu_seqlens_k, q_pos_offsets=None, topk: int = 2048,

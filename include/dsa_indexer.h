@@ -138,6 +138,39 @@ int dsa_indexer_topk(const dsa_indexer_shape* shape, const void* q, const void* 
                      hipStream_t stream);
 
 /*
+ * Prepared runner (flashinfer PR #8691, description and commit messages: the prepared call form
+ * beside the eager entry; the runner zeroes its ticket word once when it prepares and every
+ * run leaves it at zero; a new runner is made when a shape or a tensor binding changes, values
+ * may change freely; the prepare-time zero is queued on the prepare stream, so a run on another
+ * stream must be ordered after it).
+ *
+ * dsa_indexer_prepare binds the shape, every tensor pointer, topk and a workspace of at least
+ * dsa_indexer_prepared_workspace_size(shape) bytes (the top-k workspace followed by the plan).
+ * It validates the arguments like dsa_indexer_topk (same error codes), then enqueues on `stream`
+ * one small kernel that zeroes the workspace's control block (no dsa_indexer_workspace_init is
+ * needed) and stores the work decomposition derived from the segment tables' current contents,
+ * with a copy of those contents.  dsa_indexer_run enqueues only the scan's two kernels with the
+ * arguments built at prepare time: no argument checks, no device queries.  Results are exactly
+ * those of dsa_indexer_topk on the bound tensors' contents at the time of the run: the score
+ * kernel compares the live segment tables with the stored copy and derives the plan itself if
+ * they differ, so every value, the tables' included, may change between runs.
+ *   - The runner owns no device memory; it must be destroyed with dsa_indexer_runner_destroy
+ *     (host memory only).  The bound buffers must outlive it.
+ *   - Runs of one runner (or of runners sharing a workspace) must not overlap.  After a run
+ *     that returned DSA_ERR_LAUNCH, prepare again.
+ *   - dsa_indexer_run_ex times the two kernels like dsa_indexer_topk_ex (profiler may be NULL).
+ */
+typedef struct dsa_indexer_runner dsa_indexer_runner;
+size_t dsa_indexer_prepared_workspace_size(const dsa_indexer_shape* shape);
+int dsa_indexer_prepare(const dsa_indexer_shape* shape, const void* q, const void* k, const float* w,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        const int32_t* q_pos_offsets, int32_t topk, int32_t* out_ids,
+                        float* out_scores, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream, dsa_indexer_runner** runner);
+int dsa_indexer_run(dsa_indexer_runner* runner, hipStream_t stream);
+int dsa_indexer_runner_destroy(dsa_indexer_runner* runner);
+
+/*
  * dsa_indexer_topk for callers that cannot allocate device memory or own a workspace: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
  * results and errors as dsa_indexer_topk, without the workspace: the control block and score
@@ -281,6 +314,9 @@ int dsa_indexer_topk_ex(const dsa_indexer_shape* shape, const void* q, const voi
                         float* out_scores, void* workspace, size_t workspace_bytes,
                         hipStream_t stream, const dsa_indexer_tuning* tuning,
                         dsa_indexer_profiler* profiler);
+
+/* dsa_indexer_run with an optional profiler (NULL = none). */
+int dsa_indexer_run_ex(dsa_indexer_runner* runner, hipStream_t stream, dsa_indexer_profiler* profiler);
 
 /*
  * dsa_indexer_backward with an optional profiler: for backward calls the two figures a

@@ -134,6 +134,30 @@ def test_scores_argument_errors():
                                 16, None) == -4                            # no room for the control block
 
 
+def test_prepare_argument_errors():
+    L = ix.lib()
+    V = ctypes.c_void_p
+    s = ix.make_shape(16, 64, 1, 64)
+    q, k, w, cq, ck, _, oi, osc, ws = GOOD
+    h = V()
+
+    def call(shape=s, q_=q, topk=16, wsb=1 << 40, out=ctypes.byref(h)):
+        return L.dsa_indexer_prepare(ctypes.byref(shape), V(q_), V(k), V(w), V(cq), V(ck), None, topk, V(oi),
+                                     V(osc), V(ws), wsb, None, out)
+    assert call(out=None) == -1
+    assert call(q_=None) == -1 and not h.value
+    assert call(q_=0x10008) == -2
+    assert call(topk=0) == -3
+    assert call(shape=ix.make_shape(16, 70000, 2, 0)) == -3
+    # the prepared workspace adds the plan (header, table copies, tile and unit prefixes) to the
+    # top-k workspace; one byte less is rejected
+    need = ix.prepared_workspace_size(16, 64, 1, 64)
+    assert need > ix.workspace_size(16, 64, 1, 64) and need % 256 == 0
+    assert call(wsb=need - 1) == -4
+    assert L.dsa_indexer_run(None, None) == -1
+    assert L.dsa_indexer_runner_destroy(None) == -1
+
+
 def test_profiler_argument_errors():
     L = ix.lib()
     h = ctypes.c_void_p()
