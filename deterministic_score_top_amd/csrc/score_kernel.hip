@@ -53,6 +53,7 @@ constexpr int kWaitVm = 0x0F70;
 constexpr int kSlotInts = 16;
 constexpr int kSegSortMax = 256;     // batches with more segments keep table order
 constexpr int kUnitsPerBlock = 4;    // a unit holds at most ~1/4 of a resident block's share
+constexpr int kGuidedMin = 32;       // batches of only long tiles: guided chunks down to 1/32 of a share
 constexpr int kMinChunkTiles = 2;    // smallest automatic key chunk, in key tiles
 constexpr int kMaxChunkSearch = 32;  // candidate chunks tried for small batches
 constexpr int kPartEntries = kScoreThreads + 4;
@@ -132,6 +133,15 @@ __device__ void block_scan_excl(uint32_t* arr, int n, uint32_t* part) {
   __syncthreads();
 }
 
+// Guided chunk (in key tiles) of tile g of ntiles: half of a block's share of the work that
+// remains from tile g on (ntiles - g tiles of about `full` key tiles each), between `lo` and
+// `full` (a whole tile).
+__device__ __forceinline__ uint32_t guided_chunk(int g, int ntiles, uint32_t grid, int full, int lo) {
+  const uint32_t rest = (uint32_t)(ntiles - g) * (uint32_t)full;
+  const uint32_t c = (rest + 2u * grid - 1u) / (2u * grid);
+  return min((uint32_t)full, max((uint32_t)lo, c));
+}
+
 // The work decomposition of a batch (every block of a launch derives the same one from the
 // segment tables; the plan kernel derives it once for a prepared runner): validates the tables,
 // orders segments longest tile first, counts each query tile's key tiles, picks the key chunk
@@ -141,6 +151,8 @@ struct PlanInfo {
   uint32_t units;
   int ntiles;
   int chunk_tiles;
+  int guided_tiles;  // > 0: tile g's chunk is guided_chunk(g) (see there), else chunk_tiles
+  int guided_min;
   bool whole_tiles;  // every tile is exactly one unit
   int flags;         // bit 0: invalid tables, bit 1: a segment longer than Lmax
 };
@@ -172,6 +184,7 @@ __device__ PlanInfo compute_plan(const ScoreParams& p, uint32_t grid, int* slot,
   uint32_t units = 0;
   int ntiles = 0;
   int chunk_keys = kTileKeys;
+  int guided = 0, guided_min = 1;
   bool whole_tiles = false;
   if (!(plan_flags & 1)) {
     // Segment order: longest tile first (the key is the first tile's key-tile count), ties by
@@ -214,9 +227,10 @@ __device__ PlanInfo compute_plan(const ScoreParams& p, uint32_t grid, int* slot,
     if (tid == 0) {
       slot[3] = 0;
       slot[6] = 0;
+      slot[10] = -1;
     }
     __syncthreads();
-    uint32_t work = 0, kt_max = 0;
+    uint32_t work = 0, kt_max = 0, kt_min = 0xffffffffu;
     for (int g = tid; g < ntiles; g += kScoreThreads) {
       const int j = upper_bound_u32(seg_tp, B + 1, (uint32_t)g) - 1;
       const int b = (int)seg_ord[j];
@@ -230,13 +244,16 @@ __device__ PlanInfo compute_plan(const ScoreParams& p, uint32_t grid, int* slot,
       unit_pf[g] = kt;
       work += kt;
       kt_max = max(kt_max, kt);
+      if (kt) kt_min = min(kt_min, kt);
     }
-    // integer sum and max: order-free; one LDS atomic per wave
+    // integer sum, max and min: order-free; one LDS atomic per wave
     work = wave_sum(work);
     kt_max = wave_max(kt_max);
+    kt_min = wave_min(kt_min);
     if (lane == 0) {
       atomicAdd(reinterpret_cast<uint32_t*>(&slot[3]), work);
       atomicMax(reinterpret_cast<uint32_t*>(&slot[6]), kt_max);
+      atomicMin(reinterpret_cast<uint32_t*>(&slot[10]), kt_min);
     }
     __syncthreads();
     // Key chunk per work unit, in key tiles: forced by the caller, else chosen from the batch.
@@ -248,6 +265,14 @@ __device__ PlanInfo compute_plan(const ScoreParams& p, uint32_t grid, int* slot,
     // the longest split into pieces of nearly equal size.  (Measured: long-document batches
     // run 15-18 % faster than with whole tiles; causal batches and the CP tail prefer whole
     // tiles by 1-2 %.)
+    // When even the shortest tile is long next to the share (every query of the batch sees about
+    // as many keys: a CP tail), whole tiles leave each block two or three units of equal size,
+    // and a block displaced by foreign work leaves a whole unit for a second round (measured:
+    // CP tail 1.32x slower with one CU held).  Then chunks are guided (guided self-scheduling):
+    // tile g is cut in pieces of half the per-block share of the work that remains from it on,
+    // whole tiles while that is at least a tile, shrinking to 1/32 of a share at the end, so
+    // blocks that finish early take the small pieces and the last round is short, while most
+    // units stay long (each unit start reloads the query block).
     // Small batches (no more query tiles than blocks) instead take the smallest chunk that
     // still fits the whole batch in one round of units, one per block: each unit start costs
     // a query-block load, so a second round of short units is slower than longer units
@@ -275,6 +300,9 @@ __device__ PlanInfo compute_plan(const ScoreParams& p, uint32_t grid, int* slot,
         const uint32_t bound = max(share / kUnitsPerBlock, (uint32_t)kMinChunkTiles);
         const uint32_t m = (longest + bound - 1) / bound;
         chunk_tiles = (int)max((longest + m - 1) / m, 1u);
+      } else if ((uint32_t)slot[10] > share / 8u) {
+        guided = (int)longest;
+        guided_min = (int)max(share / kGuidedMin, (uint32_t)kMinChunkTiles);
       }
     }
     chunk_keys = chunk_tiles * kTileKeys;
@@ -282,7 +310,8 @@ __device__ PlanInfo compute_plan(const ScoreParams& p, uint32_t grid, int* slot,
     __syncthreads();
     bool one_each = true;  // every tile is exactly one unit (keyless tiles have none)
     for (int g = tid; g < ntiles; g += kScoreThreads) {
-      const uint32_t nu = (unit_pf[g] + chunk_tiles - 1) / chunk_tiles;
+      const uint32_t ct = guided ? guided_chunk(g, ntiles, grid, guided, guided_min) : (uint32_t)chunk_tiles;
+      const uint32_t nu = (unit_pf[g] + ct - 1) / ct;
       unit_pf[g] = nu;
       one_each &= nu == 1u;
     }
@@ -296,6 +325,8 @@ __device__ PlanInfo compute_plan(const ScoreParams& p, uint32_t grid, int* slot,
   info.units = units;
   info.ntiles = ntiles;
   info.chunk_tiles = chunk_keys / kTileKeys;
+  info.guided_tiles = guided;
+  info.guided_min = guided_min;
   info.whole_tiles = whole_tiles;
   info.flags = plan_flags;
   return info;
@@ -305,7 +336,7 @@ __device__ PlanInfo compute_plan(const ScoreParams& p, uint32_t grid, int* slot,
 // tables the plan was derived from (cu_q[B+1], cu_k[B+1], offsets[B]) and then seg_tp[B+1],
 // seg_ord[B], unit_pf[ntiles+1].
 constexpr int kPlanUnits = 0, kPlanTiles = 1, kPlanChunk = 2, kPlanWhole = 3, kPlanFlags = 4, kPlanGrid = 5,
-              kPlanB = 6, kPlanHeader = 16;
+              kPlanB = 6, kPlanGuided = 7, kPlanGuidedMin = 8, kPlanHeader = 16;
 
 __device__ __forceinline__ int plan_tables_at(int B) { return kPlanHeader; }
 __device__ __forceinline__ int plan_arrays_at(int B) { return kPlanHeader + 3 * B + 2; }
@@ -332,6 +363,8 @@ __device__ bool load_plan(const ScoreParams& p, int* slot, uint32_t* seg_tp, uin
   info.units = hdr[kPlanUnits];
   info.ntiles = (int)hdr[kPlanTiles];
   info.chunk_tiles = (int)hdr[kPlanChunk];
+  info.guided_tiles = (int)hdr[kPlanGuided];
+  info.guided_min = (int)hdr[kPlanGuidedMin];
   info.whole_tiles = hdr[kPlanWhole] != 0;
   info.flags = (int)hdr[kPlanFlags];
   const uint32_t* const arr = p.plan + plan_arrays_at(B);
@@ -371,6 +404,8 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
   const uint32_t units = info.units;
   const int ntiles = info.ntiles;
   const int chunk_keys = info.chunk_tiles * kTileKeys;
+  const int guided = info.guided_tiles;
+  const int guided_min = info.guided_min;
   const bool whole_tiles = info.whole_tiles;
   // this call's verdict on its tables, for the select kernel (always overwritten, so a bad call
   // does not affect later calls on the same workspace)
@@ -420,8 +455,9 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(ScoreParams p) 
     const int tq0 = ti * kTileQueries;
     const int nq = min(kTileQueries, lq - tq0);
     const int nmax = clampi(off + tq0 + nq, 0, lk);
-    const int kbeg = c * chunk_keys;
-    const int kend = min(kbeg + chunk_keys, nmax);
+    const int ck = guided ? (int)guided_chunk(g, ntiles, gridDim.x, guided, guided_min) * kTileKeys : chunk_keys;
+    const int kbeg = c * ck;
+    const int kend = min(kbeg + ck, nmax);
 
     // this wave's query (tile-local index wv): A operand for both row blocks and all 8 K-steps
     const bool qvalid = wv < nq;
@@ -637,6 +673,8 @@ __global__ __launch_bounds__(kScoreThreads) void plan_kernel(ScoreParams p, uint
     out[kPlanUnits] = info.units;
     out[kPlanTiles] = (uint32_t)info.ntiles;
     out[kPlanChunk] = (uint32_t)info.chunk_tiles;
+    out[kPlanGuided] = (uint32_t)info.guided_tiles;
+    out[kPlanGuidedMin] = (uint32_t)info.guided_min;
     out[kPlanWhole] = info.whole_tiles ? 1u : 0u;
     out[kPlanFlags] = (uint32_t)info.flags;
     out[kPlanGrid] = grid;

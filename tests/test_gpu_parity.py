@@ -340,11 +340,14 @@ def _holder():
     return h
 
 
+@pytest.mark.parametrize("name", ["causal_n1024", "split_tail"])
 @pytest.mark.parametrize("held", [1, 32])
-def test_bitwise_while_foreign_kernel_holds_cus(held):
+def test_bitwise_while_foreign_kernel_holds_cus(held, name):
     # the score kernel's blocks on held CUs start late; the resident ones take their work units
-    # from the ticket counter.  Results are bit-identical and the control block ends clean.
-    wl = W.make("causal_n1024", seed=3)
+    # from the ticket counter.  Results are bit-identical and the control block ends clean.  (The
+    # split tail's four rows are cut into one round of key-chunk units, one per block, so a
+    # displaced block's unit is one that another block must take.)
+    wl = W.make(name, seed=3)
     dev = _dev(wl)
     ws = ix.alloc_workspace(wl.T, wl.Tkv, wl.B, wl.max_seqlen_k)
     ref = _run(wl, dev, workspace=ws)
