@@ -78,6 +78,61 @@ def ingest_traffic(config, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir,
     print(json.dumps(rec))
 
 
+def _kernel_short(name):
+    """Kernel name without namespaces, return type and parameter list (template arguments kept)."""
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0].split("::")[-1]
+
+
+def trace_summary(trace_dir, pmc_dirs=()):
+    """Markdown summary of a rocprofv3 --kernel-trace run of bench.py: per workload phase (a new
+    phase starts at each control-block fill, i.e. each workspace the run allocates), per kernel:
+    dispatches, mean over all and over the last 20 (the timed calls) in microseconds.  With
+    --pmc run directories of the same command (GRBM_GUI_ACTIVE), also the mean shader clock
+    (counter cycles / kernel duration of the same dispatch)."""
+    rows = []
+    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        rows += list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    phase, per = 0, {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "ctrl_init" in name:
+            phase += 1
+            continue
+        short = _kernel_short(name)
+        per.setdefault((phase, short), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("| phase | kernel | dispatches | mean (us) | mean of the last 20 (us) |")
+    print("|---:|---|---:|---:|---:|")
+    for (ph, k), v in sorted(per.items()):
+        print(f"| {ph} | {k} | {len(v)} | {sum(v) / len(v):.2f} | {sum(v[-20:]) / len(v[-20:]):.2f} |")
+    for d in pmc_dirs:
+        recs = []
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            recs += list(csv.DictReader(open(path)))
+        by = {}
+        for r in recs:
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                by.setdefault(_kernel_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        trace = {}
+        for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+            for r in csv.DictReader(open(path)):
+                trace.setdefault(_kernel_short(r["Kernel_Name"]), []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+        # the counter is summed over the GPU's XCCs, each counting its own engine-clock cycles
+        nxcc = 1
+        for path in glob.glob(os.path.join(d, "**", "*agent_info.csv"), recursive=True):
+            for r in csv.DictReader(open(path)):
+                if r.get("Agent_Type") == "GPU":
+                    nxcc = max(nxcc, int(r.get("Num_Xcc") or 1))
+        for k, cyc in sorted(by.items()):
+            if k in trace and len(trace[k]) == len(cyc):
+                clk = [c / nxcc / t / 1e9 for c, t in zip(cyc, trace[k]) if t > 0]
+                print(f"\n{os.path.basename(d.rstrip('/'))}: {k}: GRBM_GUI_ACTIVE / {nxcc} XCCs / duration = "
+                      f"{sum(clk) / len(clk):.3f} GHz mean over {len(clk)} dispatches "
+                      f"(min {min(clk):.3f}, max {max(clk):.3f})")
+
+
 def copy_calibration(reps=5):
     """A plain device-to-device copy of COPY_BYTES, for counter calibration under rocprofv3."""
     import torch
@@ -424,9 +479,15 @@ def main():
                     help="time the backward of the scores (dq, dk, dw) instead of the top-k call")
     ap.add_argument("--attention", action="store_true",
                     help="time the sparse attention over the selected ids instead of the top-k call")
+    ap.add_argument("--trace-summary", nargs="+", metavar="DIR",
+                    help="print a markdown summary of a rocprofv3 --kernel-trace directory (then optional "
+                         "--pmc GRBM_GUI_ACTIVE --kernel-trace directories for the shader clock) and exit")
     ap.add_argument("--ingest-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write the score-kernel traffic record from rocprofv3 --pmc output directories")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary[0], args.trace_summary[1:])
+        return
     if args.ingest_pmc:
         ingest_traffic(args.config, *args.ingest_pmc, kernel="attention" if args.attention else "score")
         return
