@@ -21,7 +21,9 @@
 // same softmax reference; the O rows and the partial sums l of a head stay consistent.
 //   * Gathered rows land in LDS by buffer loads that write LDS directly (one 16-byte chunk per
 //     lane; an id outside [0, Tkv) becomes an out-of-range offset that reads zeros), two
-//     stages: the next tile is in flight while one is multiplied.
+//     stages: the next tile is in flight while one is multiplied.  The 18 load rounds of the
+//     next tile are issued between the MFMAs of the current tile's score product, so their
+//     address arithmetic runs while the matrix unit works.
 //   * Once every wave has finished its score product, the last 64 dims of the tile's rows
 //     (needed only for the scores) hold the P exchange.
 //   * Online softmax per lane (head) in the exp2 domain.  The reference maximum of a head only
@@ -30,7 +32,8 @@
 //   * P rounded to BF16 is the A operand of O += P . V, whose V operand is read key-major from
 //     the gathered tile by ds_read_b64_tr_b16.
 //   * The valid ids of a row are packed in order to the front of its list first, so -1 entries
-//     (the padding of rows with fewer visible keys than k) take no tiles.
+//     (the padding of rows with fewer visible keys than k) take no tiles, and only a row's last
+//     tile needs the mask of its -1 entries.
 //   * A batch of few rows splits each row's tiles into equal parts over several blocks; each part
 //     writes its unnormalised O, reference maximum and sum per head, and a second kernel
 //     combines the parts in part order.
@@ -175,7 +178,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
 #pragma unroll
     for (int st = 0; st < kQkSteps; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 16 * st);
   }
-  int ntile;
+  int ntile, total;
   {
     uint32_t cnt = 0;
     int bad = 0;
@@ -191,20 +194,21 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
     const uint32_t incl = wave_incl_scan(cnt);
     if (lane == 63) g_xchg[wv] = __uint_as_float(incl);   // the wave's count, as bits
     __syncthreads();
-    uint32_t before = 0, total = 0;
+    uint32_t before = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const uint32_t c = __float_as_uint(g_xchg[w]);
       before += w < wv ? c : 0u;
-      total += c;
+      tot += c;
     }
+    total = (int)tot;
     int pos = (int)(before + incl - cnt);
 #pragma unroll
     for (int k = 0; k < kIdsPerLane; ++k) {
       if (idr[k] >= 0) ids[pos++] = idr[k];
     }
-    ntile = ((int)total + kAttnTile - 1) / kAttnTile;
-    for (int j = (int)total + tid; j < ntile * kAttnTile; j += kAttnThreads) ids[j] = -1;
+    ntile = (total + kAttnTile - 1) / kAttnTile;
+    for (int j = total + tid; j < ntile * kAttnTile; j += kAttnThreads) ids[j] = -1;
   }
   // this block's tiles: part `part` of `split` equal ranges (empty when the row is short)
   const int tper = (ntile + p.split - 1) / p.split;
@@ -214,21 +218,24 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
 
   const __amdgpu_buffer_rsrc_t kvrs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.kv), (short)0, p.Tkv * kRowBytes, kRsrcWord3);
-  // Gather slots: load r of wave wv fills chunk slots (r*4 + wv)*64 .. +63 of a stage; slot ->
+  const __amdgpu_buffer_rsrc_t kvrs_none =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.kv), (short)0, 0, kRsrcWord3);
+  // Gather slots: load round r of wave wv fills chunk slots (r*4 + wv)*64 .. +63 of a stage; slot ->
   // (row, position), and the lane fetches the logical chunk the swizzle stores at that position.
-  auto gather = [&](unsigned char* base, int kt) __attribute__((always_inline)) {
-    int id[kLoadRounds];
-#pragma unroll
-    for (int r = 0; r < kLoadRounds; ++r) id[r] = ids[kt * kAttnTile + ((r * kWaves + wv) * 64 + lane) / kRowChunks];
-#pragma unroll
-    for (int r = 0; r < kLoadRounds; ++r) {
-      const int slot = (r * kWaves + wv) * 64 + lane;
-      const int row = slot / kRowChunks, pos = slot - row * kRowChunks;
-      const int col = ((pos & ~7) | ((pos ^ tswz(row)) & 7)) * 16;
-      const int voff = id[r] >= 0 ? id[r] * kRowBytes + col : kDropOffset;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kvrs, (__attribute__((address_space(3))) void*)(base + (r * kWaves + wv) * 1024),
-                                               16, voff, 0, 0, 0);
-    }
+  // The rounds of the next tile are issued between the MFMAs of this tile's score product.  The
+  // offset of id -1 wraps to a huge value that the clamp turns into the drop offset (a valid
+  // offset is below total_kv * 1152 < 2^31 - 16).  A step without a next tile still issues the
+  // rounds, through a descriptor of zero records (nothing is read, the free stage gets zeros).
+  auto gid = [&](int kt, int r) __attribute__((always_inline)) {
+    return ids[kt * kAttnTile + ((r * kWaves + wv) * 64 + lane) / kRowChunks];
+  };
+  auto gload = [&](unsigned char* base, __amdgpu_buffer_rsrc_t rs, int r, int id) __attribute__((always_inline)) {
+    const int slot = (r * kWaves + wv) * 64 + lane;
+    const int row = slot / kRowChunks, pos = slot - row * kRowChunks;
+    const int col = ((pos & ~7) | ((pos ^ tswz(row)) & 7)) * 16;
+    const uint32_t voff = min((uint32_t)(__mul24(id, kRowBytes) + col), (uint32_t)kDropOffset);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(base + (r * kWaves + wv) * 1024),
+                                             16, (int)voff, 0, 0, 0);
   };
 
   // transposed-read offsets of the V operand: rows (keys) 4*hf + jr (+8), columns (dims)
@@ -259,26 +266,42 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
   //
   // S^T of this wave's 32 keys; register i: key 32*kh + 8*(i/4) + 4*hf + i%4, head h0 + n.
   // Nine chunks of four K steps (ascending dims) on one accumulator.
-  auto scores = [&](const unsigned char* kb) __attribute__((always_inline)) {
+  auto scores = [&](const unsigned char* kb, unsigned char* gb, __amdgpu_buffer_rsrc_t grs, int gkt)
+      __attribute__((always_inline)) {
     auto rd = [&](int st) __attribute__((always_inline)) {
       return *reinterpret_cast<const bf16x8*>(kb + kro[st & 3] + (st >> 2) * 128);
     };
     f32x16 sp = f32x16{};
     bf16x8 ka[4], kn[4];
+    int gi[2], gn[2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) ka[j] = rd(j);
+    gi[0] = gid(gkt, 0);
+    gi[1] = gid(gkt, 1);
 #pragma unroll
     for (int c = 0; c < kQkSteps / 4; ++c) {
       if (c + 1 < kQkSteps / 4) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) kn[j] = rd(4 * (c + 1) + j);
+        gn[0] = gid(gkt, 2 * c + 2);
+        gn[1] = gid(gkt, 2 * c + 3);
       }
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sp = mfma(ka[j], qf[4 * c + j], sp);
+      sp = mfma(ka[0], qf[4 * c], sp);
+      __builtin_amdgcn_sched_barrier(0);
+      gload(gb, grs, 2 * c, gi[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      sp = mfma(ka[1], qf[4 * c + 1], sp);
+      __builtin_amdgcn_sched_barrier(0);
+      gload(gb, grs, 2 * c + 1, gi[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      sp = mfma(ka[2], qf[4 * c + 2], sp);
+      sp = mfma(ka[3], qf[4 * c + 3], sp);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) ka[j] = kn[j];
+      gi[0] = gn[0];
+      gi[1] = gn[1];
     }
     return sp;
   };
@@ -324,22 +347,25 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
     unsigned char* const kb = stage<S>();
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vector memory counter 0: tile kt has landed
     asm volatile("s_barrier" ::: "memory");
-    if (kt + 1 < kend) gather(stage<1 - S>(), kt + 1);
-    f32x16 sp = scores(kb);
+    const bool more = kt + 1 < kend;
+    f32x16 sp = scores(kb, stage<1 - S>(), more ? kvrs : kvrs_none, more ? kt + 1 : kt);
 
-    // mask, scale and the maximum of each head over this wave's keys
-    const i32x4* const idv = reinterpret_cast<const i32x4*>(ids + kt * kAttnTile + 32 * kh);
-    float tmax = -__builtin_inff();
+    // scale, then the maximum of each head over this wave's keys; only the last tile of a row
+    // holds -1 entries (the valid ids are packed to the front), so only it is masked
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const i32x4 iv = idv[2 * g4 + hf];   // keys 32*kh + 8*g4 + 4*hf .. +3
+    for (int i = 0; i < 16; ++i) sp[i] *= c2;
+    if ((kt + 1) * kAttnTile > total) {
+      const i32x4* const idv = reinterpret_cast<const i32x4*>(ids + kt * kAttnTile + 32 * kh);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int i = 4 * g4 + c;
-        sp[i] = iv[c] >= 0 ? sp[i] * c2 : -__builtin_inff();
-        tmax = fmaxf(tmax, sp[i]);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const i32x4 iv = idv[2 * g4 + hf];   // keys 32*kh + 8*g4 + 4*hf .. +3
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sp[4 * g4 + c] = iv[c] >= 0 ? sp[4 * g4 + c] : -__builtin_inff();
       }
     }
+    float tmax = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sp[i]);
     tmax = half_max(tmax);
     if (hf == 0) g_xchg[wv * 32 + n] = tmax;
     __builtin_amdgcn_s_waitcnt(kWaitLgkm);
@@ -400,12 +426,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(AttnParams p
     const bf16x8 qa1 = *reinterpret_cast<const bf16x8*>(kb + xpar + 16);
     half_product(1 - kh, qa0, qa1, oa);
   };
-  if (kbeg < kend) gather(stage<0>(), kbeg);
+  if (kbeg < kend) {
+#pragma unroll
+    for (int r = 0; r < kLoadRounds; ++r) gload(stage<0>(), kvrs, r, gid(kbeg, r));
+  }
   for (int kt = kbeg; kt < kend; kt += 2) {
     step(Int<0>{}, kt);
     if (kt + 1 >= kend) break;
     step(Int<1>{}, kt + 1);
   }
+  // the last step's rounds (zero records) are waited for before the block can end
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // l of each head = the pair's partial sums, key half 0 first; o = O / l (0 for a row with no
   // valid id), lse = (m + log2 l) * ln 2.  Every read of the exchanged maxima happened before
