@@ -24,7 +24,10 @@
 //     part's queries together, one query per step.  Per query: S = Q . K^T (K in VGPRs for
 //     the whole unit, Q from LDS), the BF16 operand G'' = w * g * [S > 0], and
 //     dk^T += Q^T . G'' with the Q^T operand read head-major from LDS by ds_read_b64_tr_b16.
-//     A query's 16 KiB q block thus serves 256 keys per load.  P (1, 2, 4, 8 or 16) depends
+//     A query's 16 KiB q block thus serves 256 keys per load; queries land in LDS two ahead
+//     (three separate LDS arrays, so the compiler does not wait for the prefetch before reading
+//     the current query), and the unit's sums leave through LDS one 32-dim block at a time as
+//     16-byte row stores.  P (1, 2, 4, 8 or 16) depends
 //     only on the number of keys: enough parts for about 512 units.  With P = 1 the unit
 //     writes dk itself; otherwise it writes an FP32 partial.
 //   * reduce kernels (P > 1): dk = the P partials added in a fixed pairwise tree
@@ -43,6 +46,8 @@
 // at 4 consecutive 16-bit elements; lane 4*r + e receives element e of lanes r, 4+r, 8+r and
 // 12+r.  With lane 4*j + r pointing at row k0 + j, columns c0 + 4*r .. +3, lane i of the group
 // receives column c0 + i of rows k0 .. k0+3.
+
+#include <type_traits>
 
 #include "dsa_internal.h"
 #include "wave_ops.h"
@@ -69,11 +74,29 @@ constexpr int kStages = 3;
 // dk kernel LDS stage: q of one query, the gradients of the unit's keys, w, and a landing
 // area for the waves that have no third load
 constexpr int kDkStageBytes = kTileBytes + kDkKeys * 4 + 256 + 256;
-constexpr int kDkOutStride = 132;  // floats per key row when the unit's sums leave through LDS
-constexpr int kDkOutBytes = kWavesB * 32 * kDkOutStride * 4;
 constexpr int kScratchInts = 16;
+// dk output: per wave and value block of 32 dims, 32 key rows of 36 floats (16-byte aligned rows,
+// at most two lanes per bank when a wave writes one dim of its 32 keys)
+constexpr int kDkOutRow = 36;
+constexpr int kDkOutWave = 32 * kDkOutRow * 4;
+constexpr int kDkStageArray = kDkStageBytes > 4 * kDkOutWave ? kDkStageBytes : 4 * kDkOutWave;
 
 static_assert(kBwdThreads == 512 && kBwdKeyTile == 64, "layout assumes 8 waves and 64-key tiles");
+template <int V>
+using Int = std::integral_constant<int, V>;
+
+// The dk kernel's stages are separate LDS arrays used with compile-time indices (the stage loop
+// is unrolled by three): the compiler can then tell that the loads into one stage do not write
+// the stage being read, and does not wait for the prefetched query before reading the current
+// one.
+__shared__ __align__(16) unsigned char g_dk0[kDkStageArray];
+__shared__ __align__(16) unsigned char g_dk1[kDkStageArray];
+__shared__ __align__(16) unsigned char g_dk2[kDkStageArray];
+__shared__ __align__(16) int g_dk_scratch[kScratchInts];
+template <int S>
+__device__ __forceinline__ unsigned char* dk_stage() {
+  return S == 0 ? g_dk0 : S == 1 ? g_dk1 : g_dk2;
+}
 static_assert(kDkKeys == 32 * kWavesB, "32 keys per wave in the dk kernel");
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -390,9 +413,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p) {
 // dk (or its partials)
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dk_kernel(BwdParams p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int kStageArea = kStages * kDkStageBytes > kDkOutBytes ? kStages * kDkStageBytes : kDkOutBytes;
-  int* const scratch = reinterpret_cast<int*>(smem + kStageArea);
+  int* const scratch = g_dk_scratch;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hf = lane >> 5;
@@ -432,26 +453,28 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dk_kernel(BwdParams p) {
   }
 
   // stage layout: q (16 KiB) | gradients of the 256 keys | w | landing area
-  auto qst = [&](int s) { return smem + s * kDkStageBytes; };
-  auto gst = [&](int s) { return smem + s * kDkStageBytes + kTileBytes; };
-  auto wst = [&](int s) { return smem + s * kDkStageBytes + kTileBytes + kDkKeys * 4; };
-  auto dst_ = [&](int s) { return smem + s * kDkStageBytes + kTileBytes + kDkKeys * 4 + 256; };
+  auto gst = [&](unsigned char* st) { return st + kTileBytes; };
+  auto wst = [&](unsigned char* st) { return st + kTileBytes + kDkKeys * 4; };
+  auto dst_ = [&](unsigned char* st) { return st + kTileBytes + kDkKeys * 4 + 256; };
   // every wave issues 3 loads per query: 2 x 1 KiB of q, then gradients (waves 0-3), w (wave 4)
   // or nothing useful (a zero-length load into the landing area)
-  auto load_query = [&](int s, int it) {
-    const int i = pbeg + it;
+  // Every step issues one query's loads (past the unit's last query through zero-record
+  // descriptors), so the count in flight is the same on every path and the waits can name it.
+  auto load_query = [&](unsigned char* s, int it) {
+    const bool real = it < iters;
+    const int i = pbeg + (real ? it : 0);
     const int64_t t = (int64_t)cq + i;
     const int nv = clampi(off + i + 1, 0, lk);
-    const __amdgpu_buffer_rsrc_t qrs = rsrc(p.q + t * (kHeads * kDim), kTileBytes);
-    unsigned char* const qd = qst(s);
+    const __amdgpu_buffer_rsrc_t qrs = rsrc(p.q + t * (kHeads * kDim), real ? kTileBytes : 0);
+    unsigned char* const qd = s;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int id = r * kWavesB + wv;
       const int row = 4 * id + (lane >> 4), pos = lane & 15;
       lds_load16(qrs, qd + id * 1024, row * kRowBytes + ((pos ^ swzbits(row)) << 4));
     }
-    if (wv < 4) lds_load4(rsrc(p.grad + t * p.ld, nv * 4), gst(s) + wv * 256, (j0 + 64 * wv + lane) * 4);
-    else if (wv == 4) lds_load4(rsrc(p.w + t * kHeads, kHeads * 4), wst(s), lane * 4);
+    if (wv < 4) lds_load4(rsrc(p.grad + t * p.ld, real ? nv * 4 : 0), gst(s) + wv * 256, (j0 + 64 * wv + lane) * 4);
+    else if (wv == 4) lds_load4(rsrc(p.w + t * kHeads, real ? kHeads * 4 : 0), wst(s), lane * 4);
     else lds_load4(rsrc(p.w, 0), dst_(s), lane * 4);
   };
   constexpr int kLoadsPerQuery = 3;
@@ -528,47 +551,52 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dk_kernel(BwdParams p) {
         dka[mb] = mfma(lds_tr_pair(qb + st * 16 * kRowBytes + trq1[mb], qb + st * 16 * kRowBytes + trq2[mb]), gb[st],
                        dka[mb]);
   };
-  auto step = [&](int c, int it) {
-    if (it + 2 < iters) load_query((c + 2) % kStages, it + 2);
-    query(qst(c));
-    if (it + 2 < iters) __builtin_amdgcn_s_waitcnt(kWaitVm | kLoadsPerQuery);
-    else __builtin_amdgcn_s_waitcnt(kWaitVm);
+  auto step = [&](auto C_, int it) {
+    constexpr int C = decltype(C_)::value;
+    load_query(dk_stage<(C + 2) % kStages>(), it + 2);
+    query(dk_stage<C>());
+    __builtin_amdgcn_s_waitcnt(kWaitVm | kLoadsPerQuery);   // query it + 1 has landed
     asm volatile("s_barrier" ::: "memory");
   };
 
   if (iters > 0) {
-    load_query(0, 0);
-    if (iters > 1) load_query(1, 1);
-    if (iters > 1) __builtin_amdgcn_s_waitcnt(kWaitVm | kLoadsPerQuery);
-    else __builtin_amdgcn_s_waitcnt(kWaitVm);
+    load_query(dk_stage<0>(), 0);
+    load_query(dk_stage<1>(), 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVm | kLoadsPerQuery);
     asm volatile("s_barrier" ::: "memory");
-    for (int it = 0; it < iters; it += kStages) {
-      step(0, it);
-      if (it + 1 < iters) step(1, it + 1);
-      if (it + 2 < iters) step(2, it + 2);
+    // whole rounds of three steps without a branch inside, then the remainder
+    int it = 0;
+    for (; it + kStages <= iters; it += kStages) {
+      step(Int<0>{}, it);
+      step(Int<1>{}, it + 1);
+      step(Int<2>{}, it + 2);
     }
+    if (it < iters) step(Int<0>{}, it);
+    if (it + 1 < iters) step(Int<1>{}, it + 1);
+    // the last steps' loads (zero records) are waited for before the stages are reused
+    __builtin_amdgcn_s_waitcnt(kWaitVm);
   }
 
-  // The unit's sums leave through LDS so that rows are written with 16-byte stores: wave wv
-  // puts register i of dka[mb] (dim 32*mb + 8*(i/4) + 4*hf + i%4 of key 32*wv + n) at
-  // row n, column dim of its own 32-row region.
+  // The unit's sums leave through LDS so that rows are written with 16-byte stores, one value
+  // block of 32 dims at a time: wave wv puts register i of dka[mb] (dim 32*mb + 8*(i/4) +
+  // 4*hf + i%4 of key 32*wv + n) at row n, column dim - 32*mb of its own region (waves 0-3 in
+  // stage 0, 4-7 in stage 1), then reads the region back by rows.
   __syncthreads();
-  float* const ob = reinterpret_cast<float*>(smem) + wv * 32 * kDkOutStride;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      ob[n * kDkOutStride + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3)] = dka[mb][i];
-  __syncthreads();
+  float* const ob = reinterpret_cast<float*>(wv < 4 ? dk_stage<0>() : dk_stage<1>()) + (wv & 3) * 32 * kDkOutRow;
   const int nkeys = min(32, lk_all - j0 - 32 * wv);
   float* const out = (parts == 1 ? p.dk : p.part + (int64_t)part * p.Tkv * kDim) +
                      ((int64_t)ck + j0 + 32 * wv) * kDim;
 #pragma unroll
-  for (int rep = 0; rep < 16; ++rep) {
-    const int e = rep * 64 + lane;
-    const int key = e >> 5, c4 = e & 31;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(ob + key * kDkOutStride + 4 * c4);
-    if (key < nkeys) *reinterpret_cast<f32x4*>(out + (int64_t)key * kDim + 4 * c4) = v;
+  for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ob[n * kDkOutRow + 8 * (i >> 2) + 4 * hf + (i & 3)] = dka[mb][i];
+#pragma unroll
+    for (int rep = 0; rep < 4; ++rep) {
+      const int e = rep * 64 + lane;
+      const int key = e >> 3, c4 = e & 7;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(ob + key * kDkOutRow + 4 * c4);
+      if (key < nkeys) *reinterpret_cast<f32x4*>(out + (int64_t)key * kDim + 32 * mb + 4 * c4) = v;
+    }
   }
 }
 
@@ -622,10 +650,8 @@ __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const float* __restr
 }  // namespace
 
 size_t bwd_dq_smem_bytes() { return kStages * kDqStageBytes + kScratchInts * 4; }
-size_t bwd_dk_smem_bytes() {
-  const size_t area = kStages * kDkStageBytes > kDkOutBytes ? kStages * kDkStageBytes : kDkOutBytes;
-  return area + kScratchInts * 4;
-}
+// the dk kernel uses static LDS only
+size_t bwd_dk_smem_bytes() { return 0; }
 
 int bwd_dk_parts(int64_t total_k) {
   const int64_t blocks = (total_k + kDkKeys - 1) / kDkKeys;
@@ -643,11 +669,8 @@ int bwd_dq_parts(int64_t total_q) {
 }
 
 hipError_t bwd_prepare() {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_dq_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bwd_dq_smem_bytes());
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_dk_kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bwd_dk_smem_bytes());
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_dq_kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bwd_dq_smem_bytes());
 }
 
 hipError_t launch_backward(const BwdParams& p, int dq_grid, int dk_grid, int cus, hipStream_t s,
