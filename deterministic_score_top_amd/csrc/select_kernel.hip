@@ -13,21 +13,28 @@
 //      overwhelming probability, theta is below the k-th key while only a few hundred keys
 //      more than k are >= theta (the sample is kept in LDS for its histogram when it fits);
 //   B  one pass compares every key with theta and copies the survivors (key, position) into
-//      per-wave LDS regions in position order (ballots + mbcnt, no atomics);
+//      per-wave LDS regions in position order (one ballot + mbcnt per key slot, no atomics);
+//      the rest of a region's last 256-entry step is filled with key 0, below every survivor,
+//      so the passes below read whole steps without masks;
 //   C  the exact k-th key T is found over the survivors with range-normalised LDS histograms
-//      (digits of up to 10 bits; once the bin holding rank k has at most 64 keys, one wave
-//      ranks them directly), together with how many keys equal T and how many of those are
-//      left out (the lowest positions);
+//      (1024 bins per pass) until the bin holding rank k has at most 64 keys or one value;
+//      one more pass counts, per wave, the keys above that bin and gathers the bin's keys,
+//      which one wave ranks directly: T, how many keys equal T, how many of those are left
+//      out (the lowest positions), and each wave's count of selected and equal keys;
 //   D  the survivors are written in position order: wave w starts at the fixed-order sum of
-//      the selected counts of waves 0..w-1, lanes are ranked with ballots and mbcnt.
+//      the selected counts of waves 0..w-1, lanes are ranked with ballots and mbcnt; a wave
+//      that keeps all or none of its keys equal to T decides each key with one comparison.
 // If the sample's guess fails (fewer than k survivors, or a region overflows), an exact
 // fallback resolves T with histograms over every key and writes from the whole row.  Results
 // never depend on which path ran.
 //
 // Passes read the row from the workspace rows written by the score phase (L2/MALL-resident
 // for rows of moderate length).  A row costs about 1.25 reads when the sample's guess holds.
-// Wave reductions and scans use DPP lane moves; row loads are range-checked buffer loads
-// issued several steps at a time.  The first workgroup also checks and resets the work-unit
+// Lane l of a wave reads keys 64 apart (positions base + 256*s + 64*c + l), so every load is
+// a coalesced 256-byte dword load and the keys of a step are in position order c by c; loads
+// are range-checked buffer loads (keys past the row read as 0) issued four steps at a time.
+// Wave reductions and scans use DPP lane moves.  Output rows are written through
+// range-checked buffer stores.  The first workgroup also checks and resets the work-unit
 // counter the score kernel left in the control block.
 
 #include "dsa_internal.h"
@@ -45,23 +52,22 @@ constexpr int kCandCapWide = 4096;  // the same for 1024-thread rows (16 waves, 
 constexpr int kSegCache = 256;    // segments whose tables are cached in LDS
 constexpr int kSampleStride = 4;  // sample = every key of every 4th step
 constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor word 3: raw 32-bit data, range-checked
+constexpr int kRankMax = 64;      // a bin with at most this many keys is ranked directly
 
 __device__ __forceinline__ float key_value(uint32_t key) {
   const uint32_t u = key ^ (~(uint32_t)((int32_t)key >> 31) | 0x80000000u);
   return __uint_as_float(u);
 }
 
-__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+// base + the number of set mask bits below this lane
+__device__ __forceinline__ uint32_t ballot_rank(uint64_t mask, uint32_t base) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, base));
 }
 
-// Exclusive prefix (over lanes) and total of a per-lane count in 0..7.
-__device__ __forceinline__ void wave_prefix3(uint32_t cnt, uint32_t& excl, uint32_t& total) {
-  const uint64_t b0 = __ballot(cnt & 1u), b1 = __ballot(cnt & 2u), b2 = __ballot(cnt & 4u);
-  excl = lanes_below(b0) + 2u * lanes_below(b1) + 4u * lanes_below(b2);
-  total = (uint32_t)__popcll(b0) + 2u * (uint32_t)__popcll(b1) + 4u * (uint32_t)__popcll(b2);
-}
+__device__ __forceinline__ uint32_t popc(uint64_t mask) { return (uint32_t)__popcll(mask); }
+
+__device__ __forceinline__ uint32_t sub_sat(uint32_t a, uint32_t b) { return __builtin_elementwise_sub_sat(a, b); }
 
 
 // Segment tables of batches with at most kSegCache segments, cached in LDS by every block.
@@ -203,34 +209,35 @@ __device__ void find_bin(SM& sm, int nb, uint32_t krem) {
   __syncthreads();
 }
 
-// Row keys seen by one lane: positions base + 256*s + 4*lane + c of the wave's span, read from
-// the row on every pass (the rows stay L2/MALL-resident between passes).  Loads are buffer loads
-// range-checked at round_up(n, 4) keys (the row stride is a multiple of 64 keys, so that bound
-// stays inside the row): vectors past it read as zero, keys past n inside the last vector are
-// masked, so no load sits under a branch and a batch of loads can be in flight together.
+// Row keys seen by one lane: step s of the wave's span covers positions base + 256*s + 64*c + lane
+// (c = 0..3), so that for each c the wave reads 256 contiguous bytes and the four keys of a step
+// are in position order when taken c by c.  Loads are dword buffer loads range-checked at n keys:
+// positions at or past n read as 0, which is below every real key, so no load sits under a branch
+// and a batch of loads can be in flight together.
 struct Keys {
   __amdgpu_buffer_rsrc_t rs;
-  int n, base, span;
+  int base, span;
 
-  __device__ void load4(int pos, uint32_t (&o)[4]) const {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, pos * 4, 0, 0);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) o[c] = (pos + c < n) ? (uint32_t)v[c] : 0u;
-  }
-  // f(position of c=0, keys[4]) for every `stride`-th step of the span, in order (wave-uniform).
-  // Steps are loaded kBatch at a time before any is used.
-  template <class F>
-  __device__ void each(F&& f, int stride = 1) const {
+  // f(step s, position of this lane's c = 0 key, keys[4]) for every `stride`-th step of the span,
+  // in order (wave-uniform).  Steps are loaded kBatch at a time before any is used.
+  template <int kStride = 1, class F>
+  __device__ void each(F&& f) const {
     constexpr int kBatch = 4;
     const int lane = threadIdx.x & 63;
     const int steps = span >> 8;
-    for (int s = 0; s < steps; s += kBatch * stride) {
+    for (int s = 0; s < steps; s += kBatch * kStride) {
       uint32_t t[kBatch][4];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) load4(base + 256 * (s + u * stride) + 4 * lane, t[u]);
+      // one lane offset per batch; the step and c offsets are instruction immediates when they fit
+      int off = (base + 256 * s + lane) * 4;
+      asm("" : "+v"(off));  // keeps the offsets as immediates on this base (no loop-carried end pointer)
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
-        if (s + u * stride < steps) f(base + 256 * (s + u * stride) + 4 * lane, t[u]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          t[u][c] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 1024 * kStride * u + 256 * c, 0, 0);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (s + u * kStride < steps) f(s + u * kStride, base + 256 * (s + u * kStride) + lane, t[u]);
     }
   }
 };
@@ -241,7 +248,7 @@ template <int NT, class KS>
 __device__ void resolve_all(Smem<NT>& sm, const KS& ks, int topk, uint32_t& T, uint32_t& eq_skip) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   uint32_t mn = 0xffffffffu, mx = 0u, cnt = 0;
-  ks.each([&](int, const uint32_t (&k4)[4]) {
+  ks.each([&](int, int, const uint32_t (&k4)[4]) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       mn = min(mn, k4[c] - 1u);  // invalid (0) wraps to the top and drops out
@@ -277,7 +284,7 @@ __device__ void resolve_all(Smem<NT>& sm, const KS& ks, int topk, uint32_t& T, u
     const uint32_t nb = 1u << bits;
     for (int i = tid; i < (int)nb; i += NT) sm.hist[i] = 0u;
     __syncthreads();
-    ks.each([&](int, const uint32_t (&k4)[4]) {
+    ks.each([&](int, int, const uint32_t (&k4)[4]) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const uint32_t v = k4[c] - kmin;
@@ -296,15 +303,13 @@ __device__ void resolve_all(Smem<NT>& sm, const KS& ks, int topk, uint32_t& T, u
   T = kmin + prefix;
   eq_skip = eq_total - krem;
   uint32_t gt = 0, eq = 0;
-  ks.each([&](int, const uint32_t (&k4)[4]) {
+  ks.each([&](int, int, const uint32_t (&k4)[4]) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      gt += (k4[c] && k4[c] > T) ? 1u : 0u;
-      eq += (k4[c] && k4[c] == T) ? 1u : 0u;
+      gt += popc(__ballot(k4[c] > T));  // T >= kmin >= 1: padding keys (0) are neither
+      eq += popc(__ballot(k4[c] == T));
     }
   });
-  gt = wave_sum(gt);
-  eq = wave_sum(eq);
   if (lane == 0) {
     sm.wred[wv][2] = gt;
     sm.wred[wv][3] = eq;
@@ -328,6 +333,16 @@ __device__ void wave_bases(SM& sm, uint32_t eq_skip, uint32_t& sel_base, uint32_
     }
   }
 }
+
+// Output row stores: range-checked at topk entries (a store past them is dropped).
+struct OutRow {
+  __amdgpu_buffer_rsrc_t ids, scores;
+  int kb;
+  __device__ void put(uint32_t slot, int pos, uint32_t key) const {
+    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(kb + pos), ids, (int)(slot * 4u), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key_value(key)), scores, (int)(slot * 4u), 0, 0);
+  }
+};
 
 template <int NT>
 __global__ __launch_bounds__(NT, NT == 256 ? 6 : 1) void select_kernel(SelectParams p) {
@@ -353,46 +368,49 @@ __global__ __launch_bounds__(NT, NT == 256 ? 6 : 1) void select_kernel(SelectPar
     }
 
     Keys ks;
-    ks.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(row), (short)0, ((n + 3) & ~3) * 4,
-                                              kRsrcWord3);
-    ks.n = n;
+    ks.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(row), (short)0, n * 4, kRsrcWord3);
     ks.span = ((n + NW * 256 - 1) / (NW * 256)) * 256;
     ks.base = wv * ks.span;
+    const int steps = ks.span >> 8;
+    OutRow out;
+    out.ids = __builtin_amdgcn_make_buffer_rsrc(oid, (short)0, topk * 4, kRsrcWord3);
+    out.scores = __builtin_amdgcn_make_buffer_rsrc(osc, (short)0, topk * 4, kRsrcWord3);
+    out.kb = kb;
 
     // ---- A: threshold from a sample: every key of every 4th step of each wave's span --------
     for (int i = tid; i < kHistBins; i += NT) sm.hist[i] = 0u;  // free since the last row's barriers
     // The wave's sample also goes to its (still unused) survivor region when it fits, so the
     // histogram pass below reads it from LDS instead of from the row again.
-    const int sample_steps = ((ks.span >> 8) + kSampleStride - 1) / kSampleStride;
+    const int sample_steps = (steps + kSampleStride - 1) / kSampleStride;
     const bool staged = sample_steps * 256 <= R;
-    uint32_t smin = 0xffffffffu, smax = 0u, scnt = 0;
-    ks.each([&](int pos, const uint32_t (&k4)[4]) {
+    uint32_t smin = 0xffffffffu, smax = 0u;
+    ks.template each<kSampleStride>([&](int s, int, const uint32_t (&k)[4]) {
       if (staged) {
-        const int idx = ((pos - ks.base) >> 8) / kSampleStride;  // sampled step of this lane's keys
-        *reinterpret_cast<u32x4*>(&sm.ckey[wv][idx * 256 + 4 * lane]) = u32x4{k4[0], k4[1], k4[2], k4[3]};
-      }
+        uint32_t* const st = &sm.ckey[wv][(s / kSampleStride) * 256 + lane];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        smin = min(smin, k4[c] - 1u);  // invalid (0) wraps to the top and drops out
-        smax = max(smax, k4[c]);
-        scnt += k4[c] ? 1u : 0u;
+        for (int c = 0; c < 4; ++c) st[64 * c] = k[c];
       }
-    }, kSampleStride);
+      smin = min(smin, min(k[0] - 1u, k[1] - 1u));  // invalid (0) wraps to the top and drops out
+      smin = min(smin, min(k[2] - 1u, k[3] - 1u));
+      smax = max(smax, max(k[0], k[1]));
+      smax = max(smax, max(k[2], k[3]));
+    });
     smin = wave_min(smin);
     smax = wave_max(smax);
-    scnt = wave_sum(scnt);
     if (lane == 0) {
       sm.wred[wv][4] = smin;
       sm.wred[wv][5] = smax;
-      sm.wred[wv][6] = scnt;
     }
-    __syncthreads();
+    // sample size: the sampled positions below n (every key below n is a real key)
     uint32_t m = 0;
+    for (int w = 0; w < NW; ++w)
+      for (int s = 0; s < steps; s += kSampleStride)
+        m += (uint32_t)min(max(n - (w * ks.span + 256 * s), 0), 256);
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       smin = min(smin, sm.wred[i][4]);
       smax = max(smax, sm.wred[i][5]);
-      m += sm.wred[i][6];
     }
     smin += 1u;
     // sample rank whose bin edge becomes theta: k*m/n plus 4 standard deviations and a margin
@@ -403,19 +421,19 @@ __global__ __launch_bounds__(NT, NT == 256 ? 6 : 1) void select_kernel(SelectPar
       const uint32_t srange = smax - smin;
       const int sbits = 32 - __clz((int)srange);
       const int sshift = max(sbits - kHistBits, 0);
-      auto bin_sample = [&](const uint32_t (&k4)[4]) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (k4[c]) atomicAdd(&sm.hist[(k4[c] - smin) >> sshift], 1u);
-      };
+      // invalid keys (0) saturate into bin 0, the lowest: they cannot move the bin of rank r < m
+      auto bin_sample = [&](uint32_t k) { atomicAdd(&sm.hist[sub_sat(k, smin) >> sshift], 1u); };
       if (staged) {
         for (int idx = 0; idx < sample_steps; ++idx) {
           const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.ckey[wv][idx * 256 + 4 * lane]);
-          const uint32_t k4[4] = {v[0], v[1], v[2], v[3]};
-          bin_sample(k4);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) bin_sample(v[c]);
         }
       } else {
-        ks.each([&](int, const uint32_t (&k4)[4]) { bin_sample(k4); }, kSampleStride);
+        ks.template each<kSampleStride>([&](int, int, const uint32_t (&k)[4]) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) bin_sample(k[c]);
+        });
       }
       __syncthreads();
       find_bin<NT>(sm, kHistBins, r);  // ends with a barrier: the histogram is free afterwards
@@ -426,31 +444,26 @@ __global__ __launch_bounds__(NT, NT == 256 ? 6 : 1) void select_kernel(SelectPar
     // the histogram is free again: clear it for the first digit pass over the survivors
     for (int i = tid; i < kHistBins; i += NT) sm.hist[i] = 0u;
     uint32_t run = 0, rmax = 0;
-    ks.each([&](int pos, const uint32_t (&k4)[4]) {
-      uint32_t cnt = 0;
+    ks.each([&](int, int pos, const uint32_t (&k)[4]) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        cnt += k4[c] >= theta ? 1u : 0u;
-        rmax = max(rmax, k4[c]);
-      }
-      uint32_t ex, tot;
-      wave_prefix3(cnt, ex, tot);
-      if (tot) {
-        uint32_t slot = run + ex;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if (k4[c] >= theta) {
-            if (slot < (uint32_t)R) {
-              sm.ckey[wv][slot] = k4[c];
-              sm.cpos[wv][slot] = (uint16_t)(pos + c);
-            }
-            ++slot;
-          }
+        const bool keep = k[c] >= theta;
+        const uint64_t km = __ballot(keep);
+        const uint32_t slot = ballot_rank(km, run);
+        if (keep && slot < (uint32_t)R) {
+          sm.ckey[wv][slot] = k[c];
+          sm.cpos[wv][slot] = (uint16_t)(pos + 64 * c);
         }
+        run += popc(km);
       }
-      run += tot;
+      rmax = max(rmax, max(max(k[0], k[1]), max(k[2], k[3])));
     });
     rmax = wave_max(rmax);
+    const uint32_t mine = min(run, (uint32_t)R);
+    {  // key 0 (below every survivor) in the rest of the last 256-entry step the passes read
+      const uint32_t end = min((mine + 255u) & ~255u, (uint32_t)R);
+      for (uint32_t i = mine + lane; i < end; i += 64) sm.ckey[wv][i] = 0u;
+    }
     if (lane == 0) {
       sm.wred[wv][7] = run;
       sm.wred[wv][8] = rmax;
@@ -465,10 +478,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 6 : 1) void select_kernel(SelectPar
       cmax = max(cmax, sm.wred[i][8]);
       overflow |= sm.wred[i][7] > (uint32_t)R;
     }
-    const uint32_t mine = min(run, (uint32_t)R);
-    // entries i0 + 64c + lane (c = 0..3) of this wave's region, all four read before any is
-    // used; the region holds a whole number of 256-entry steps, so the reads stay inside it
-    // (entries at or past `mine` are stale and masked by the callers)
+    // entries i0 + 64c + lane (c = 0..3) of this wave's region, all four read before any is used
     auto cand4 = [&](uint32_t i0, uint32_t (&kk)[4]) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) kk[c] = sm.ckey[wv][i0 + 64 * c + lane];
@@ -477,17 +487,16 @@ __global__ __launch_bounds__(NT, NT == 256 ? 6 : 1) void select_kernel(SelectPar
     uint32_t T, eq_skip, sel_base, eq_base;
     if (!overflow && total >= (uint32_t)topk) {
       // ---- C: exact k-th key among the survivors ---------------------------------------------
-      // cmax (the row maximum) is a survivor, so [theta, cmax] spans every survivor
-      const uint32_t range = cmax - theta;
-      int shift = range ? 32 - __clz((int)range) : 0;
-      uint32_t prefix = 0, krem = (uint32_t)topk, eq_total = total;
+      // [lo, top] is the key range holding rank krem (from the top) of the survivors, cnt keys.
+      // cmax (the row maximum) is a survivor, so [theta, cmax] holds every survivor.  Each
+      // digit pass splits the range into 1024 bins and keeps the bin holding rank krem.
+      uint32_t lo = theta, top = cmax, krem = (uint32_t)topk, cnt = total;
       bool first = true;
-      while (shift > 0) {
-        const int bits = min(kHistBits, shift);
-        shift -= bits;
-        const uint32_t nb = 1u << bits;
+      while (lo != top && (first || cnt > (uint32_t)kRankMax)) {
+        const uint32_t width = top - lo;
+        const int shift = max(32 - __clz((int)width) - kHistBits, 0);
         if (!first) {  // the first pass uses the histogram cleared during compaction
-          for (int i = tid; i < (int)nb; i += NT) sm.hist[i] = 0u;
+          for (int i = tid; i < kHistBins; i += NT) sm.hist[i] = 0u;
           __syncthreads();
         }
         for (uint32_t i0 = 0; i0 < mine; i0 += 256) {
@@ -495,95 +504,141 @@ __global__ __launch_bounds__(NT, NT == 256 ? 6 : 1) void select_kernel(SelectPar
           cand4(i0, kk);
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const uint32_t v = kk[c] - theta;
-            if (i0 + 64 * c + lane < mine && (first || (uint32_t)((uint64_t)v >> (shift + bits)) == prefix))
-              atomicAdd(&sm.hist[(v >> shift) & (nb - 1u)], 1u);
+            const uint32_t v = kk[c] - lo;  // keys below lo (and padding) wrap past width
+            if (v <= width) atomicAdd(&sm.hist[v >> shift], 1u);
           }
         }
         __syncthreads();
-        find_bin<NT>(sm, (int)nb, krem);
-        prefix = (prefix << bits) | sm.bcast[0];
+        find_bin<NT>(sm, kHistBins, krem);
+        const uint32_t b = sm.bcast[0];
         krem -= sm.bcast[1];
-        eq_total = sm.bcast[2];
+        cnt = sm.bcast[2];
+        lo += b << shift;
+        const uint64_t bin_top = (uint64_t)lo + ((1ull << shift) - 1ull);
+        top = bin_top < (uint64_t)top ? (uint32_t)bin_top : top;
         first = false;
-        if (shift > 0 && eq_total <= 64u) {
-          // Few keys left in the bin: rank them directly.  Gather them (any order) and let lane
-          // i of wave 0 count how many are greater / greater-or-equal than key i.
-          for (uint32_t i0 = 0; i0 < mine; i0 += 256) {
-            uint32_t kk[4];
-            cand4(i0, kk);
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-              if (i0 + 64 * c + lane < mine && ((kk[c] - theta) >> shift) == prefix)
-                sm.hist[atomicAdd(&sm.bcast[3], 1u)] = kk[c];
-          }
-          __syncthreads();
-          if (wv == 0) {
-            const uint32_t c = eq_total;
-            const uint32_t mykey = (uint32_t)lane < c ? sm.hist[lane] : 0u;
-            uint32_t gt = 0, ge = 0;
-            for (uint32_t j = 0; j < c; ++j) {
-              const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mykey, (int)j);
-              gt += o > mykey ? 1u : 0u;
-              ge += o >= mykey ? 1u : 0u;
-            }
-            if ((uint32_t)lane < c && gt < krem && krem <= ge) {  // every such lane holds the same key
-              sm.bcast[4] = mykey;
-              sm.bcast[5] = gt;
-              sm.bcast[6] = ge - gt;
-            }
-          }
-          __syncthreads();
-          prefix = sm.bcast[4] - theta;
-          krem -= sm.bcast[5];
-          eq_total = sm.bcast[6];
-          shift = 0;
-        }
       }
-      T = theta + prefix;
-      eq_skip = eq_total - krem;
-      uint32_t gt = 0, eq = 0;
+      // One pass: per wave, the keys above the bin and in it; when the bin spans several key
+      // values (then it holds at most kRankMax keys) its keys are gathered with their wave.
+      const bool rank = lo != top;
+      const uint32_t width = top - lo;
+      uint32_t gtw = 0, inw = 0;
       for (uint32_t i0 = 0; i0 < mine; i0 += 256) {
         uint32_t kk[4];
         cand4(i0, kk);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const bool live = i0 + 64 * c + lane < mine;
-          gt += live && kk[c] > T ? 1u : 0u;
-          eq += live && kk[c] == T ? 1u : 0u;
+          const uint64_t am = __ballot(kk[c] > top);
+          const bool inb = kk[c] - lo <= width;
+          const uint64_t bm = __ballot(inb);
+          gtw += popc(am);
+          inw += popc(bm);
+          if (rank && bm) {
+            uint32_t g0 = 0;
+            if (lane == 0) g0 = atomicAdd(&sm.bcast[3], popc(bm));
+            g0 = (uint32_t)__builtin_amdgcn_readlane((int)g0, 0);
+            const uint32_t g = ballot_rank(bm, g0);
+            if (inb && g < (uint32_t)kRankMax) {
+              sm.hist[g] = kk[c];
+              sm.hist[kRankMax + g] = (uint32_t)wv;
+            }
+          }
         }
       }
-      gt = wave_sum(gt);
-      eq = wave_sum(eq);
       if (lane == 0) {
-        sm.wred[wv][2] = gt;
-        sm.wred[wv][3] = eq;
+        sm.wred[wv][2] = gtw;
+        sm.wred[wv][3] = inw;
       }
       __syncthreads();
+      uint32_t eq_total;
+      if (rank) {
+        // lane i of wave 0 ranks gathered key i against the others; the lane whose rank range
+        // holds krem has T.  Per wave: the bin's keys above T join its count above, and its keys
+        // equal to T replace its count in the bin.
+        if (wv == 0) {
+          const uint32_t c = cnt;
+          const uint32_t mykey = (uint32_t)lane < c ? sm.hist[lane] : 0u;
+          const uint32_t mywv = (uint32_t)lane < c ? sm.hist[kRankMax + lane] : 0xffffffffu;
+          // key 0 (below every gathered key) after the last one, so whole 4-key groups are read
+          if ((uint32_t)lane < 4u) sm.hist[c + lane] = 0u;
+          uint32_t gt = 0, ge = 0;
+          for (uint32_t j = 0; j < c; j += 4) {  // every lane reads the same 16 bytes: a broadcast
+            const u32x4 o = *reinterpret_cast<const u32x4*>(&sm.hist[j]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              gt += o[q] > mykey ? 1u : 0u;
+              ge += o[q] >= mykey ? 1u : 0u;
+            }
+          }
+          const uint64_t tm = __ballot((uint32_t)lane < c && gt < krem && krem <= ge);
+          const int tl = (int)__builtin_ctzll(tm);
+          const uint32_t tv = (uint32_t)__builtin_amdgcn_readlane((int)mykey, tl);
+          const uint32_t tgt = (uint32_t)__builtin_amdgcn_readlane((int)gt, tl);
+          const uint32_t tge = (uint32_t)__builtin_amdgcn_readlane((int)ge, tl);
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            const uint32_t g2 = popc(__ballot(mywv == (uint32_t)w && mykey > tv));
+            const uint32_t e2 = popc(__ballot(mywv == (uint32_t)w && mykey == tv));
+            if (lane == 0) {
+              sm.wred[w][2] += g2;
+              sm.wred[w][3] = e2;
+            }
+          }
+          if (lane == 0) {
+            sm.bcast[4] = tv;
+            sm.bcast[5] = tge - tgt;
+            sm.bcast[6] = krem - tgt;
+          }
+        }
+        __syncthreads();
+        T = sm.bcast[4];
+        eq_total = sm.bcast[5];
+        krem = sm.bcast[6];
+      } else {
+        T = lo;
+        eq_total = cnt;
+      }
+      eq_skip = eq_total - krem;
       wave_bases<NT>(sm, eq_skip, sel_base, eq_base);
       // ---- D: ordered write from the survivors ------------------------------------------------
-      uint32_t eq_run = eq_base, sel_run = sel_base;
-      for (uint32_t i0 = 0; i0 < mine; i0 += 256) {
-        uint32_t kk[4];
-        int pos[4];
-        cand4(i0, kk);
+      const uint32_t eq_w = sm.wred[wv][3];
+      uint32_t sel_run = sel_base;
+      if (eq_w == 0u || eq_base >= eq_skip || eq_base + eq_w <= eq_skip) {
+        // this wave keeps all or none of its keys equal to T: one comparison decides
+        const uint32_t tc = (eq_w != 0u && eq_base + eq_w <= eq_skip) ? T : T - 1u;  // T >= theta >= 1
+        for (uint32_t i0 = 0; i0 < mine; i0 += 256) {
+          uint32_t kk[4];
+          int pos[4];
+          cand4(i0, kk);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) pos[c] = sm.cpos[wv][i0 + 64 * c + lane];
+          for (int c = 0; c < 4; ++c) pos[c] = sm.cpos[wv][i0 + 64 * c + lane];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {  // entries i0 + 64c + lane: region order
-          const bool live = i0 + 64 * c + lane < mine;
-          const bool eqf = live && kk[c] == T;
-          const bool gtf = live && kk[c] > T;
-          const uint64_t eqm = __ballot(eqf);
-          const bool self = gtf || (eqf && eq_run + lanes_below(eqm) >= eq_skip);
-          const uint64_t selm = __ballot(self);
-          const uint32_t slot = sel_run + lanes_below(selm);
-          if (self && slot < (uint32_t)topk) {  // exactly topk are selected; the bound is a guard
-            oid[slot] = kb + pos[c];
-            osc[slot] = key_value(kk[c]);
+          for (int c = 0; c < 4; ++c) {
+            const bool self = kk[c] > tc;
+            const uint64_t sm_ = __ballot(self);
+            if (self) out.put(ballot_rank(sm_, sel_run), pos[c], kk[c]);
+            sel_run += popc(sm_);
           }
-          eq_run += (uint32_t)__popcll(eqm);
-          sel_run += (uint32_t)__popcll(selm);
+        }
+      } else {
+        // keys > T, and the keys equal to T whose rank among the row's equal keys is >= eq_skip
+        uint32_t eq_run = eq_base;
+        for (uint32_t i0 = 0; i0 < mine; i0 += 256) {
+          uint32_t kk[4];
+          int pos[4];
+          cand4(i0, kk);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) pos[c] = sm.cpos[wv][i0 + 64 * c + lane];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const bool eqf = kk[c] == T;
+            const uint64_t em = __ballot(eqf);
+            const bool self = kk[c] > T || (eqf && ballot_rank(em, eq_run) >= eq_skip);
+            const uint64_t sm_ = __ballot(self);
+            if (self) out.put(ballot_rank(sm_, sel_run), pos[c], kk[c]);
+            eq_run += popc(em);
+            sel_run += popc(sm_);
+          }
         }
       }
     } else {
@@ -591,39 +646,17 @@ __global__ __launch_bounds__(NT, NT == 256 ? 6 : 1) void select_kernel(SelectPar
       resolve_all<NT>(sm, ks, topk, T, eq_skip);
       wave_bases<NT>(sm, eq_skip, sel_base, eq_base);
       uint32_t eq_run = eq_base, sel_run = sel_base;
-      ks.each([&](int pos, const uint32_t (&k4)[4]) {
-        bool eqf[4], gtf[4];
-        uint32_t eqc = 0;
+      ks.each([&](int, int pos, const uint32_t (&k)[4]) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          eqf[c] = k4[c] && k4[c] == T;
-          gtf[c] = k4[c] && k4[c] > T;
-          eqc += eqf[c] ? 1u : 0u;
+          const bool eqf = k[c] == T;  // T >= 1: padding keys (0) are never equal to it
+          const uint64_t em = __ballot(eqf);
+          const bool self = k[c] > T || (eqf && ballot_rank(em, eq_run) >= eq_skip);
+          const uint64_t sm_ = __ballot(self);
+          if (self) out.put(ballot_rank(sm_, sel_run), pos + 64 * c, k[c]);
+          eq_run += popc(em);
+          sel_run += popc(sm_);
         }
-        uint32_t eq_ex, eq_tot;
-        wave_prefix3(eqc, eq_ex, eq_tot);
-        bool self[4];
-        uint32_t selc = 0;
-        uint32_t er = eq_run + eq_ex;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          self[c] = gtf[c] || (eqf[c] && er >= eq_skip);
-          er += eqf[c] ? 1u : 0u;
-          selc += self[c] ? 1u : 0u;
-        }
-        uint32_t sel_ex, sel_tot;
-        wave_prefix3(selc, sel_ex, sel_tot);
-        uint32_t slot = sel_run + sel_ex;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if (self[c] && slot < (uint32_t)topk) {
-            oid[slot] = kb + pos + c;
-            osc[slot] = key_value(k4[c]);
-            ++slot;
-          }
-        }
-        eq_run += eq_tot;
-        sel_run += sel_tot;
       });
     }
   }
