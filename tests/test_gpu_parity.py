@@ -99,6 +99,16 @@ def test_select_long_rows_exact(distinct, nk, topk):
     _check_all(wl, exact=True)
 
 
+def test_select_region_overflow_random_rows():
+    # Gaussian scores on rows of 3073 to 3330 keys with topk = 2048, 160 rows (the 256-thread
+    # select blocks): each wave reads a span of 1024 positions (the last wave only the rest), so
+    # about three quarters of a span survive the sampled threshold and the three full waves
+    # overflow their 768-entry survivor regions -- these rows take the exact fallback over the
+    # whole row, without ties deciding anything
+    wl = W.random_segments([80, 80], [3400, 3400], [3072, 3250], topk=2048, seed=77)
+    _check_all(wl)
+
+
 @pytest.mark.parametrize("distinct", [None, 16, 2, 1])
 @pytest.mark.parametrize("nk", [3000, 6000, 12000])
 def test_select_many_long_rows_exact(distinct, nk):
