@@ -91,24 +91,38 @@ __device__ bool cache_segments(const SelectParams& p, SegCache& sc) {
 }
 
 // Visible key count n and first key id kb of row t (both wave-uniform); n = 0 when the call's
-// tables are invalid.
+// tables are invalid.  The cached tables are read from LDS and the others from global memory on
+// separate paths, each value made scalar on its own path: a read through a pointer that may be
+// either would be a flat load, whose wait also waits for this wave's outstanding output stores.
 __device__ void row_geometry(const SelectParams& p, const SegCache& sc, bool cached, bool bad, int t,
                              int& n_out, int& kb_out) {
   int n = 0, kb = 0;
   if (!bad) {
-    const int32_t* cq = cached ? sc.cq : p.cu_q;
-    int lo = 0, hi = p.B + 1;  // first segment start beyond t
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (cq[mid] <= t) lo = mid + 1; else hi = mid;
-    }
-    const int b = lo - 1;
-    if (b >= 0 && b < p.B) {
-      const int qb = cq[b];
-      kb = cached ? sc.ck[b] : p.cu_k[b];
-      const int lk = min((cached ? sc.ck[b + 1] : p.cu_k[b + 1]) - kb, p.Lmax);
-      const int off = cached ? sc.off[b] : (p.offs ? p.offs[b] : 0);
-      n = min(max(off + (t - qb) + 1, 0), max(lk, 0));
+    auto geometry = [&](auto get) {
+      int lo = 0, hi = p.B + 1;  // first segment start beyond t
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (get(0, mid) <= t) lo = mid + 1; else hi = mid;
+      }
+      const int b = lo - 1;
+      if (b >= 0 && b < p.B) {
+        const int qb = get(0, b);
+        kb = get(1, b);
+        const int lk = min(get(1, b + 1) - kb, p.Lmax);
+        const int off = get(2, b);
+        n = min(max(off + (t - qb) + 1, 0), max(lk, 0));
+      }
+    };
+    if (cached) {
+      geometry([&](int which, int i) {
+        const int v = which == 0 ? sc.cq[i] : which == 1 ? sc.ck[i] : sc.off[i];
+        return __builtin_amdgcn_readfirstlane(v);
+      });
+    } else {
+      geometry([&](int which, int i) {
+        const int v = which == 0 ? p.cu_q[i] : which == 1 ? p.cu_k[i] : (p.offs ? p.offs[i] : 0);
+        return __builtin_amdgcn_readfirstlane(v);
+      });
     }
   }
   n_out = __builtin_amdgcn_readfirstlane(n);  // the same for every lane: keep it scalar
