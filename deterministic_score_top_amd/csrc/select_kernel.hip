@@ -8,10 +8,11 @@
 //
 // Per row (one workgroup of 256 threads, or 1024 when the batch has few rows; workgroups loop
 // over rows):
-//   A  a sample of the row (1/4 of it) gives a threshold theta = lower edge of the sample
-//      histogram bin that holds a rank four standard deviations past k*m/n, so that, with
-//      overwhelming probability, theta is below the k-th key while only a few hundred keys
-//      more than k are >= theta (the sample is kept in LDS for its histogram when it fits);
+//   A  a sample of the row (1/4 of it, 1/8 for 1024-thread rows) gives a threshold theta =
+//      lower edge of the sample histogram bin that holds a rank four standard deviations past
+//      k*m/n, so that, with overwhelming probability, theta is below the k-th key while only a
+//      few hundred keys more than k are >= theta (the sample is kept in LDS for its histogram
+//      when it fits);
 //   B  one pass compares every key with theta and copies the survivors (key, position) into
 //      per-wave LDS regions in position order (one ballot + mbcnt per key slot, no atomics);
 //      the rest of a region's last 256-entry step is filled with key 0, below every survivor,
@@ -50,7 +51,7 @@ constexpr int kHistBins = 1 << kHistBits;
 constexpr int kCandCap = 3072;    // survivors per row held in LDS (256-thread rows)
 constexpr int kCandCapWide = 4096;  // the same for 1024-thread rows (16 waves, 256 each)
 constexpr int kSegCache = 256;    // segments whose tables are cached in LDS
-constexpr int kSampleStride = 4;  // sample = every key of every 4th step
+constexpr int kSampleStride = 4;  // sample = every key of every 4th step (every 8th for 1024-thread rows)
 constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor word 3: raw 32-bit data, range-checked
 constexpr int kRankMax = 64;      // a bin with at most this many keys is ranked directly
 
@@ -395,12 +396,15 @@ __global__ __launch_bounds__(NT, NT == 256 ? 6 : 1) void select_kernel(SelectPar
     for (int i = tid; i < kHistBins; i += NT) sm.hist[i] = 0u;  // free since the last row's barriers
     // The wave's sample also goes to its (still unused) survivor region when it fits, so the
     // histogram pass below reads it from LDS instead of from the row again.
-    const int sample_steps = (steps + kSampleStride - 1) / kSampleStride;
+    // 1024-thread rows (few-row batches) are latency-bound: a sparser sample shortens the wait for
+    // the slowest of 16 waves' sample loads, and their 4096 survivor slots hold the wider margin
+    constexpr int kSS = NT >= 1024 ? 2 * kSampleStride : kSampleStride;
+    const int sample_steps = (steps + kSS - 1) / kSS;
     const bool staged = sample_steps * 256 <= R;
     uint32_t smin = 0xffffffffu, smax = 0u;
-    ks.template each<kSampleStride>([&](int s, int, const uint32_t (&k)[4]) {
+    ks.template each<kSS>([&](int s, int, const uint32_t (&k)[4]) {
       if (staged) {
-        uint32_t* const st = &sm.ckey[wv][(s / kSampleStride) * 256 + lane];
+        uint32_t* const st = &sm.ckey[wv][(s / kSS) * 256 + lane];
 #pragma unroll
         for (int c = 0; c < 4; ++c) st[64 * c] = k[c];
       }
@@ -418,7 +422,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 6 : 1) void select_kernel(SelectPar
     // sample size: the sampled positions below n (every key below n is a real key)
     uint32_t m = 0;
     for (int w = 0; w < NW; ++w)
-      for (int s = 0; s < steps; s += kSampleStride)
+      for (int s = 0; s < steps; s += kSS)
         m += (uint32_t)min(max(n - (w * ks.span + 256 * s), 0), 256);
     __syncthreads();
 #pragma unroll
@@ -444,7 +448,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 6 : 1) void select_kernel(SelectPar
           for (int c = 0; c < 4; ++c) bin_sample(v[c]);
         }
       } else {
-        ks.template each<kSampleStride>([&](int, int, const uint32_t (&k)[4]) {
+        ks.template each<kSS>([&](int, int, const uint32_t (&k)[4]) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) bin_sample(k[c]);
         });

@@ -109,6 +109,23 @@ def test_select_region_overflow_random_rows():
     _check_all(wl)
 
 
+FEW_LONG = [
+    # q_lens, k_lens, offsets, topk: at most a quarter as many rows as CUs (the 1024-thread select
+    # blocks with their sparser sample) and rows of 16 500 to 65 536 keys
+    ([8], [60000], [59992], 2048),
+    ([3, 5], [17000, 40000], [16997, 39995], 2048),
+    ([6], [30000], [29994], 256),
+    ([4], [65536], [65532], 1000),
+    ([2, 2, 2], [16500, 33000, 50000], [16498, 32998, 49998], 2048),
+]
+
+
+@pytest.mark.parametrize("case", range(len(FEW_LONG)))
+def test_few_long_rows(case):
+    ql, kl, offs, topk = FEW_LONG[case]
+    _check_all(W.random_segments(ql, kl, offs, topk=topk, seed=500 + case))
+
+
 @pytest.mark.parametrize("distinct", [None, 16, 2, 1])
 @pytest.mark.parametrize("nk", [3000, 6000, 12000])
 def test_select_many_long_rows_exact(distinct, nk):
