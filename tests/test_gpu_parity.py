@@ -320,6 +320,18 @@ def test_full_config_sampled(name):
             assert np.array_equal(ids[t], oi[r][:wl.topk]), t
 
 
+@pytest.mark.parametrize("name", ["causal_n8192", "cp_tail", "zigzag16"])
+@pytest.mark.parametrize("tuning", [dict(grid_blocks=97), dict(key_chunk_tiles=5), dict(key_chunk_tiles=1, grid_blocks=300)])
+def test_full_config_chunking_and_grid_bitwise(name, tuning):
+    # the full shapes under other work decompositions: an odd grid (other guided chunks on the CP
+    # tail, other chunk sizes on the long-document shares) and forced key chunks give the same bits
+    wl = W.make(name)
+    dev = _dev(wl)
+    a = _run(wl, dev)
+    b = _run(wl, dev, tuning=tuning)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
 def test_weight_power_of_two_scaling_bitwise():
     # w x 2^j scales every FP32 partial sum by 2^j exactly: scores scale bit-exactly, ids are unchanged
     wl = W.random_segments([40, 9, 77], [300, 50, 1000], [200, 0, 900], topk=64, seed=40)
